@@ -1,0 +1,289 @@
+"""fp64 CPU oracle for relative-position-bias attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library; the only thing both sides take from a common place is the seeded
+input draws in ``workloads/``.
+
+Sources, cited by page title and section (the pages give the definition in
+prose only; no listing, worked example or numbers exist for this path):
+  [S-RPB]  "SGLang と Miles が Inkling を初日からサポート" (winzheng.jp),
+           section "相対位置バイアス付き Attention".  Every query token has a
+           relative feature r besides q, k, v; a learned per-head matrix P
+           maps r to relative logits indexed by causal-distance bucket; for
+           query i, key j and head h the logit is the scaled dot product plus
+           the bias picked by the distance i-j; distances past rel_extent add
+           no bias; future keys stay causally masked.  The same section mixes
+           sliding-window and full-attention layers, and full-attention layers
+           may scale logits by a length-dependent log factor.
+  [S-ARCH] same page, section "Inkling のモデルアーキテクチャ": the bias
+           module (RelLogitsProj) adds a query-conditioned relative bias to the
+           attention logits in place of a positional embedding.
+  [V-ARCH] "vLLM TML Inkling サポート" (agentlenshq.com), section
+           "TML Inkling モデルアーキテクチャ": GQA with head size 128 in every
+           layer; the relative term is added to the logits before softmax.
+
+Readings taken where the pages leave a step open (each is one line in the
+design notes):
+  * r is one vector per token shared by all heads; P is one matrix per query
+    head, P[h] of shape [r_dim, E].
+  * The bucket of distance p-j is p-j itself; R has exactly E entries and
+    distances >= E get bias 0.
+  * scale multiplies q.k only; the bias is added unscaled.
+  * Log-scale factor f(p) = ln(p+1)/ln(base) multiplies the whole logit
+    (dot + bias); base = 0 turns it off.
+  * Window W > 0: key j visible iff 0 <= p-j < W.  W = 0: full causal.
+  * Query row t sits at position p = Skv - Sq + t.
+  * GQA: query head h reads kv head h // (Hq/Hkv).
+
+Pins (tests/test_oracle.py): brute force on tiny shapes; R = 0 against
+torch's scaled_dot_product_attention in fp64; closed forms for uniform
+weights (mean of visible v, lse = ln n), single visible key, one-hot bias
+with position-coded v, shift invariance when W <= E, and the log-scale factor
+through a two-level closed form.  The LSE combine is pinned by splitting a
+full oracle result over key ranges and recombining.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "relproj",
+    "log_scale_factor",
+    "attention",
+    "attention_rows",
+    "attention_partial",
+    "lse_combine",
+    "brute_attention",
+]
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: upcast its exact values
+        x = x.detach().to("cpu").double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def relproj(r, P):
+    """R[..., h, e] = sum_c r[..., c] * P[h, c, e]   ([S-RPB]: P projects r to
+    per-head relative logits).  r: [..., r_dim]; P: [Hq, r_dim, E]."""
+    r = _f64(r)
+    P = _f64(P)
+    Hq, r_dim, E = P.shape
+    flat = r.reshape(-1, r_dim)
+    out = np.empty((flat.shape[0], Hq, E), dtype=np.float64)
+    for h in range(Hq):
+        out[:, h, :] = flat @ P[h]
+    return out.reshape(*r.shape[:-1], Hq, E)
+
+
+def log_scale_factor(p, base: float):
+    """f(p) = ln(p+1)/ln(base) for the full-attention log-scale ([S-RPB]); 1 if off."""
+    p = np.asarray(p, dtype=np.float64)
+    if not base:
+        return np.ones_like(p)
+    return np.log(p + 1.0) / math.log(base)
+
+
+def _attend(qrows, prow, K, V, Rrows, *, window, scale, log_scale_base, key_pos=None,
+            key_lo=None, key_hi=None):
+    """Core definition for one head.
+
+    qrows [n, d]; prow [n] absolute query positions; K/V [m, d] the keys at
+    absolute positions key_pos (default 0..m-1); Rrows [n, E] or None.  Keys
+    outside [key_lo, key_hi) count as not visible (one split of a split-KV
+    decode).  Returns (o [n, d], lse [n]); a row with no visible key gets
+    o = 0 and lse = -inf.
+    """
+    j = np.arange(K.shape[0]) if key_pos is None else np.asarray(key_pos)
+    dist = prow[:, None] - j[None, :]                      # causal distance p - j
+    vis = dist >= 0                                        # future keys masked
+    if window > 0:
+        vis &= dist < window                               # sliding window: W keys incl. self
+    if key_lo is not None:
+        vis &= j[None, :] >= key_lo
+    if key_hi is not None:
+        vis &= j[None, :] < key_hi
+    s = scale * (qrows @ K.T)                              # scaled dot product
+    if Rrows is not None and Rrows.shape[1] > 0:
+        E = Rrows.shape[1]
+        in_ext = vis & (dist < E)                          # distances >= E add nothing
+        idx = np.clip(dist, 0, E - 1)
+        bias = np.take_along_axis(Rrows, idx, axis=1)      # entry for distance p - j
+        s = s + np.where(in_ext, bias, 0.0)
+    f = log_scale_factor(prow, log_scale_base)
+    s = s * f[:, None]                                     # log-scale multiplies the whole logit
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1)
+    has = np.isfinite(m)
+    m_safe = np.where(has, m, 0.0)
+    w = np.exp(s - m_safe[:, None])                        # masked keys -> exactly 0
+    l = w.sum(axis=1)
+    o = np.zeros((qrows.shape[0], V.shape[1]), dtype=np.float64)
+    o[has] = (w[has] @ V) / l[has, None]
+    lse = np.full(qrows.shape[0], -np.inf)
+    lse[has] = m[has] + np.log(l[has])
+    return o, lse
+
+
+def _prep(q, k, v, R, scale):
+    q, k, v, R = _f64(q), _f64(k), _f64(v), _f64(R)
+    B, Sq, Hq, d = q.shape
+    Bk, Skv, Hkv, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape or Hq % Hkv:
+        raise ValueError("shape mismatch")
+    if R is not None and R.shape[:3] != (B, Sq, Hq):
+        raise ValueError("R must be [B, Sq, Hq, E]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return q, k, v, R, scale
+
+
+def attention(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0, chunk=512):
+    """Full oracle.  q [B,Sq,Hq,d], k/v [B,Skv,Hkv,d], R [B,Sq,Hq,E] or None.
+
+    Returns o [B,Sq,Hq,d] and lse [B,Hq,Sq] (natural log), both fp64.
+    """
+    q, k, v, R, scale = _prep(q, k, v, R, scale)
+    B, Sq, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    o = np.zeros((B, Sq, Hq, d))
+    lse = np.zeros((B, Hq, Sq))
+    pos = Skv - Sq + np.arange(Sq)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for t0 in range(0, Sq, chunk):
+                t1 = min(t0 + chunk, Sq)
+                Rr = None if R is None else R[b, t0:t1, h]
+                oo, ll = _attend(q[b, t0:t1, h], pos[t0:t1], k[b, :, g], v[b, :, g], Rr,
+                                 window=window, scale=scale, log_scale_base=log_scale_base)
+                o[b, t0:t1, h] = oo
+                lse[b, h, t0:t1] = ll
+    return o, lse
+
+
+def attention_rows(q, k, v, R=None, rows=(), *, window=0, scale=None, log_scale_base=0.0):
+    """Oracle on selected query rows only.  rows: iterable of (b, t).
+
+    Returns o [n, Hq, d] and lse [n, Hq] for the rows in the given order.
+    q/k/v may be torch tensors of any float dtype (their exact values are
+    upcast).  R is [B, Sq, Hq, E], or a callable (b, t) -> [Hq, E], or None.
+    Only keys that can be visible to the selected rows are upcast.
+    """
+    rows = list(rows)
+    B, Sq, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = np.zeros((len(rows), Hq, d))
+    lse = np.zeros((len(rows), Hq))
+    by_b = {}
+    for i, (b, t) in enumerate(rows):
+        by_b.setdefault(int(b), []).append((i, int(t)))
+    for b, items in by_b.items():
+        idx = [i for i, _ in items]
+        ts = [t for _, t in items]
+        prow = np.array([Skv - Sq + t for t in ts])
+        qb = np.stack([_f64(q[b, t]) for t in ts])          # [n, Hq, d]
+        if R is None:
+            Rb = None
+        elif callable(R):
+            Rb = np.stack([_f64(R(b, t)) for t in ts])       # [n, Hq, E]
+        else:
+            Rb = np.stack([_f64(R[b, t]) for t in ts])
+        lo = 0 if window == 0 else max(0, int(prow.min()) - window + 1)
+        hi = int(prow.max()) + 1
+        kpos = np.arange(lo, hi)
+        for g in range(Hkv):
+            Kg = _f64(k[b, lo:hi, g])
+            Vg = _f64(v[b, lo:hi, g])
+            for hh in range(G):
+                h = g * G + hh
+                oo, ll = _attend(qb[:, h], prow, Kg, Vg, None if Rb is None else Rb[:, h],
+                                 window=window, scale=scale, log_scale_base=log_scale_base,
+                                 key_pos=kpos)
+                o[idx, h] = oo
+                lse[idx, h] = ll
+    return o, lse
+
+
+def attention_partial(q, k, v, R=None, *, key_lo, key_hi, window=0, scale=None, log_scale_base=0.0):
+    """Attention restricted to keys in [key_lo, key_hi): one split of a split-KV
+    decode.  Returns (o, lse) like ``attention``; rows with no visible key in
+    the range give o = 0 and lse = -inf."""
+    q, k, v, R, scale = _prep(q, k, v, R, scale)
+    B, Sq, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    o = np.zeros((B, Sq, Hq, d))
+    lse = np.zeros((B, Hq, Sq))
+    pos = Skv - Sq + np.arange(Sq)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            Rr = None if R is None else R[b, :, h]
+            oo, ll = _attend(q[b, :, h], pos, k[b, :, g], v[b, :, g], Rr, window=window, scale=scale,
+                             log_scale_base=log_scale_base, key_lo=key_lo, key_hi=key_hi)
+            o[b, :, h] = oo
+            lse[b, h] = ll
+    return o, lse
+
+
+def lse_combine(o_parts, lse_parts):
+    """Merge split partials: o_parts [S, ...rows, d] (each normalised within its
+    split), lse_parts [S, ...rows].  Splits with lse = -inf get weight 0.
+    Returns (o [...rows, d], lse [...rows])."""
+    o_parts = _f64(o_parts)
+    lse_parts = _f64(lse_parts)
+    M = lse_parts.max(axis=0)
+    M_safe = np.where(np.isfinite(M), M, 0.0)
+    w = np.exp(lse_parts - M_safe[None])                 # exp(-inf) = 0
+    den = w.sum(axis=0)
+    num = (w[..., None] * o_parts).sum(axis=0)
+    ok = den > 0
+    o = np.zeros_like(num)
+    o[ok] = num[ok] / den[ok][..., None]
+    lse = np.full(M.shape, -np.inf)
+    lse[ok] = M_safe[ok] + np.log(den[ok])
+    return o, lse
+
+
+def brute_attention(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0):
+    """Pure-Python loops over (b, h, t, j).  Tiny shapes only."""
+    q, k, v, R, scale = _prep(q, k, v, R, scale)
+    B, Sq, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    E = 0 if R is None else R.shape[3]
+    o = np.zeros((B, Sq, Hq, d))
+    lse = np.zeros((B, Hq, Sq))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for t in range(Sq):
+                p = Skv - Sq + t
+                f = (math.log(p + 1.0) / math.log(log_scale_base)) if log_scale_base else 1.0
+                logits = []
+                for j in range(Skv):
+                    dist = p - j
+                    if dist < 0 or (window > 0 and dist >= window):
+                        continue
+                    dot = 0.0
+                    for c in range(d):
+                        dot += q[b, t, h, c] * k[b, j, g, c]
+                    bias = R[b, t, h, dist] if (R is not None and dist < E) else 0.0
+                    logits.append((j, f * (scale * dot + bias)))
+                m = max(x for _, x in logits)
+                den = sum(math.exp(x - m) for _, x in logits)
+                for c in range(d):
+                    o[b, t, h, c] = sum(math.exp(x - m) * v[b, j, g, c] for j, x in logits) / den
+                lse[b, h, t] = m + math.log(den)
+    return o, lse

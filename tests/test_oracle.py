@@ -1,0 +1,301 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+The pages define the method in prose only ("SGLang と Miles が Inkling を初日から
+サポート", section "相対位置バイアス付き Attention"): they print no worked
+example and no numbers for it.  So every pin here is a closed form, a special
+case that reduces to a library routine, or brute force on tiny inputs, chosen
+so that a dropped term, a wrong sign or index, or a transposed operand in the
+oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (attention, attention_partial, attention_rows, brute_attention,
+                    log_scale_factor, lse_combine, relproj)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def _rand(shape, seed, std=1.0):
+    g = np.random.default_rng(seed)
+    return g.standard_normal(shape) * std
+
+
+def _case(B=1, Sq=7, Skv=7, Hq=4, Hkv=2, d=8, E=5, seed=0):
+    q = _rand((B, Sq, Hq, d), seed)
+    k = _rand((B, Skv, Hkv, d), seed + 1)
+    v = _rand((B, Skv, Hkv, d), seed + 2)
+    R = _rand((B, Sq, Hq, E), seed + 3)
+    return q, k, v, R
+
+
+# --------------------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("window,base,Sq,Skv,E,G", [
+    (0, 0.0, 9, 9, 4, 2),
+    (3, 0.0, 9, 9, 6, 2),
+    (0, 4096.0, 8, 8, 3, 1),
+    (4, 16.0, 5, 12, 7, 4),      # decode-like: queries at the bottom-right
+    (0, 0.0, 11, 11, 20, 1),     # E larger than every distance
+    (1, 0.0, 6, 6, 2, 2),
+])
+def test_oracle_matches_brute_force(window, base, Sq, Skv, E, G):
+    Hkv = 2
+    q, k, v, R = _case(B=2, Sq=Sq, Skv=Skv, Hq=Hkv * G, Hkv=Hkv, d=6, E=E, seed=window * 7 + Sq)
+    o1, l1 = attention(q, k, v, R, window=window, log_scale_base=base, chunk=4)
+    o2, l2 = brute_attention(q, k, v, R, window=window, log_scale_base=base)
+    assert np.max(np.abs(o1 - o2)) <= 1e-12
+    assert np.max(np.abs(l1 - l2)) <= 1e-12
+
+
+def test_rows_and_partial_agree_with_full():
+    q, k, v, R = _case(B=2, Sq=10, Skv=13, Hq=4, Hkv=2, d=8, E=6, seed=5)
+    for window, base in ((0, 0.0), (4, 0.0), (0, 64.0)):
+        o, l = attention(q, k, v, R, window=window, log_scale_base=base)
+        rows = [(0, 0), (1, 9), (0, 5), (1, 3)]
+        orow, lrow = attention_rows(q, k, v, R, rows, window=window, log_scale_base=base)
+        for i, (b, t) in enumerate(rows):
+            assert np.max(np.abs(orow[i] - o[b, t])) <= 1e-13
+            assert np.max(np.abs(lrow[i] - l[b, :, t])) <= 1e-13
+        op, lp = attention_partial(q, k, v, R, key_lo=0, key_hi=13, window=window, log_scale_base=base)
+        assert np.max(np.abs(op - o)) <= 1e-13
+
+
+# --------------------------------------------------------------------------- library routine
+
+@pytest.mark.parametrize("window,base", [(0, 0.0), (5, 0.0), (0, 4096.0), (3, 100.0)])
+def test_zero_bias_equals_sdpa(window, base):
+    """With no bias the method is plain causal (windowed) GQA attention:
+    torch's scaled_dot_product_attention in fp64 with an explicit mask and the
+    kv heads repeated per group.  The log-scale factor is folded into q."""
+    B, Sq, Skv, Hq, Hkv, d = 2, 11, 14, 6, 2, 16
+    q, k, v, _ = _case(B, Sq, Skv, Hq, Hkv, d, 1, seed=11)
+    o, _ = attention(q, k, v, None, window=window, log_scale_base=base)
+    o0, _ = attention(q, k, v, np.zeros((B, Sq, Hq, 9)), window=window, log_scale_base=base)
+    assert np.max(np.abs(o - o0)) <= 1e-14
+    G = Hq // Hkv
+    pos = Skv - Sq + np.arange(Sq)
+    f = np.ones(Sq) if not base else np.log(pos + 1.0) / math.log(base)
+    qt = torch.tensor(q * f[None, :, None, None]).permute(0, 2, 1, 3)
+    kt = torch.tensor(k).repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    vt = torch.tensor(v).repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    j = np.arange(Skv)
+    dist = pos[:, None] - j[None, :]
+    mask = dist >= 0
+    if window:
+        mask &= dist < window
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.tensor(mask))
+    ref = ref.permute(0, 2, 1, 3).numpy()
+    assert np.max(np.abs(o - ref)) <= 1e-12
+
+
+# --------------------------------------------------------------------------- closed forms
+
+def test_golden_closed_forms():
+    cases = json.load(open(GOLDEN))["cases"]
+    assert len(cases) >= 5
+    for c in cases:
+        S = c["S"]
+        q = np.zeros((1, S, 1, 1))
+        k = np.zeros((1, S, 1, 1))
+        v = np.array(c["v"], dtype=np.float64).reshape(1, S, 1, 1)
+        E = c["E"]
+        R = None
+        if E:
+            R = np.zeros((1, S, 1, E))
+            for dist, val in c["bias"].items():
+                R[0, :, 0, int(dist)] = val
+        o, lse = attention(q, k, v, R, window=c["window"], log_scale_base=c["log_scale_base"])
+        np.testing.assert_allclose(o[0, :, 0, 0], c["o"], rtol=0, atol=1e-13, err_msg=c["name"])
+        np.testing.assert_allclose(lse[0, 0, :], c["lse"], rtol=0, atol=1e-13, err_msg=c["name"])
+
+
+@pytest.mark.parametrize("window,Sq,Skv", [(0, 12, 12), (5, 12, 12), (1, 12, 12), (4, 3, 20), (0, 1, 30)])
+def test_uniform_weights_give_visible_mean(window, Sq, Skv):
+    """q = k = 0 and R = 0: every visible key has logit 0, so o_t is the mean of
+    the visible v (prefix sums) and lse = ln(#visible).  Pins the causal and
+    window counting and the bottom-right query alignment."""
+    Hq, Hkv, d = 4, 2, 3
+    q = np.zeros((1, Sq, Hq, d))
+    k = np.zeros((1, Skv, Hkv, d))
+    v = _rand((1, Skv, Hkv, d), 3)
+    o, lse = attention(q, k, v, np.zeros((1, Sq, Hq, 7)), window=window)
+    csum = np.concatenate([np.zeros((1, Hkv, d)), np.cumsum(v[0], axis=0)])
+    for t in range(Sq):
+        p = Skv - Sq + t
+        lo = 0 if window == 0 else max(0, p - window + 1)
+        n = p - lo + 1
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            mean = (csum[p + 1, g] - csum[lo, g]) / n
+            assert np.max(np.abs(o[0, t, h] - mean)) <= 1e-13
+            assert abs(lse[0, h, t] - math.log(n)) <= 1e-13
+
+
+def test_window_one_returns_v_and_first_row_returns_v0():
+    q, k, v, R = _case(B=1, Sq=9, Skv=9, Hq=2, Hkv=1, d=5, E=4, seed=21)
+    o, lse = attention(q, k, v, R, window=1)
+    assert np.max(np.abs(o[0, :, 0] - v[0, :, 0])) == 0.0
+    o, lse = attention(q, k, v, R, window=0, log_scale_base=4096.0)
+    assert np.max(np.abs(o[0, 0] - v[0, 0, 0][None])) == 0.0
+
+
+def test_constant_v_gives_constant_output():
+    q, k, v, R = _case(B=2, Sq=10, Skv=10, Hq=4, Hkv=2, d=4, E=6, seed=8)
+    v = np.ones_like(v) * 3.5
+    o, _ = attention(q, k, v, R * 10, window=3, log_scale_base=64.0)
+    assert np.max(np.abs(o - 3.5)) <= 1e-13
+
+
+def test_gqa_grouping_is_contiguous():
+    """Query head h reads kv head h // (Hq/Hkv): a constant v per kv head shows it."""
+    B, S, Hq, Hkv, d = 1, 6, 8, 4, 2
+    q, k, _, R = _case(B, S, S, Hq, Hkv, d, 3, seed=2)
+    v = np.zeros((B, S, Hkv, d))
+    for g in range(Hkv):
+        v[:, :, g, :] = g
+    o, _ = attention(q, k, v, R)
+    for h in range(Hq):
+        assert np.max(np.abs(o[0, :, h] - h // (Hq // Hkv))) <= 1e-13
+
+
+@pytest.mark.parametrize("dstar,window", [(0, 0), (1, 0), (63, 0), (2, 3), (5, 3)])
+def test_one_hot_bias_selects_distance(dstar, window):
+    """q = k = 0, R one-hot 30 at distance d*, v coded by position in two
+    channels: each row must pick the key at p - d* with weight >= 1 - Skv e^-30
+    (or the plain visible mean when no visible key sits at that distance)."""
+    S, E, Hq = 300, 64, 2
+    q = np.zeros((1, S, Hq, 4))
+    k = np.zeros((1, S, 1, 4))
+    v = np.zeros((1, S, 1, 4))
+    j = np.arange(S)
+    v[0, :, 0, 0] = j % 256
+    v[0, :, 0, 1] = j // 256
+    R = np.zeros((1, S, Hq, E))
+    R[..., dstar] = 30.0
+    o, _ = attention(q, k, v, R, window=window)
+    tol = 256 * S * math.exp(-30.0) * 2
+    for t in range(S):
+        lo = 0 if window == 0 else max(0, t - window + 1)
+        target = t - dstar
+        if target >= lo:
+            want = v[0, target, 0]
+        else:
+            want = v[0, lo:t + 1, 0].mean(axis=0)
+        for h in range(Hq):
+            assert np.max(np.abs(o[0, t, h] - want)) <= tol, (t, h)
+
+
+@pytest.mark.parametrize("base", [0.0, 4096.0])
+def test_shift_invariance_when_window_within_extent(base):
+    """Adding c to every R entry adds f(p)*c to every visible logit when W <= E,
+    which softmax ignores; when W > E the far keys get no shift, so o moves."""
+    q, k, v, R = _case(B=1, Sq=16, Skv=16, Hq=2, Hkv=1, d=8, E=6, seed=4)
+    o1, l1 = attention(q, k, v, R, window=6, log_scale_base=base)
+    o2, l2 = attention(q, k, v, R + 2.5, window=6, log_scale_base=base)
+    assert np.max(np.abs(o1 - o2)) <= 1e-12
+    f = log_scale_factor(np.arange(16), base)
+    assert np.max(np.abs((l2 - l1)[0] - 2.5 * f[None, :])) <= 1e-12
+    o3, _ = attention(q, k, v, R, window=0, log_scale_base=base)
+    o4, _ = attention(q, k, v, R + 2.5, window=0, log_scale_base=base)
+    assert np.max(np.abs(o3 - o4)) > 1e-3
+
+
+def test_log_scale_factor_closed_form():
+    p = np.array([0, 1, 3, 4095, 32767])
+    f = log_scale_factor(p, 4096.0)
+    assert f[0] == 0.0
+    assert abs(f[3] - 1.0) <= 1e-15
+    assert abs(f[4] - 15.0 / 12.0) <= 1e-15
+    assert abs(f[2] - 2.0 / 12.0) <= 1e-15
+    assert np.all(log_scale_factor(p, 0.0) == 1.0)
+
+
+def test_log_scale_scales_logit_including_bias():
+    """Self bias c with q = k = 0 under f(p): the self weight is e^{f(p) c}
+    against p unit weights; position-coded v gives a closed form per row."""
+    S, c, L = 40, 3.0, 8.0
+    q = np.zeros((1, S, 1, 1))
+    k = np.zeros((1, S, 1, 1))
+    v = np.arange(S, dtype=np.float64).reshape(1, S, 1, 1)
+    R = np.zeros((1, S, 1, 2))
+    R[..., 0] = c
+    o, lse = attention(q, k, v, R, log_scale_base=L)
+    for p in range(S):
+        w = math.exp(math.log(p + 1.0) / math.log(L) * c)
+        want = (w * p + p * (p - 1) / 2.0) / (w + p)
+        assert abs(o[0, p, 0, 0] - want) <= 1e-12
+        assert abs(lse[0, 0, p] - math.log(w + p)) <= 1e-12
+
+
+# --------------------------------------------------------------------------- relproj
+
+def test_relproj_one_hot_r_selects_P_row():
+    Hq, r_dim, E = 3, 5, 7
+    P = _rand((Hq, r_dim, E), 1)
+    r = np.zeros((2, 4, r_dim))
+    for t in range(4):
+        r[0, t, t] = 1.0
+        r[1, t, (t + 2) % r_dim] = -2.0
+    R = relproj(r, P)
+    assert R.shape == (2, 4, Hq, E)
+    for t in range(4):
+        assert np.array_equal(R[0, t], P[:, t, :])
+        assert np.array_equal(R[1, t], -2.0 * P[:, (t + 2) % r_dim, :])
+
+
+def test_relproj_one_hot_P_selects_r_channel():
+    Hq, r_dim, E = 4, 6, 9
+    r = _rand((3, 5, r_dim), 2)
+    P = np.zeros((Hq, r_dim, E))
+    for h in range(Hq):
+        P[h, (h + 1) % r_dim, (2 * h) % E] = h + 1.0
+    R = relproj(r, P)
+    for h in range(Hq):
+        want = np.zeros((3, 5, E))
+        want[..., (2 * h) % E] = (h + 1.0) * r[..., (h + 1) % r_dim]
+        assert np.array_equal(R[:, :, h], want)
+
+
+def test_relproj_small_brute_force():
+    Hq, r_dim, E = 2, 3, 4
+    r = _rand((1, 3, r_dim), 3)
+    P = _rand((Hq, r_dim, E), 4)
+    R = relproj(r, P)
+    for t in range(3):
+        for h in range(Hq):
+            for e in range(E):
+                s = 0.0
+                for c in range(r_dim):
+                    s += r[0, t, c] * P[h, c, e]
+                assert abs(R[0, t, h, e] - s) <= 1e-14
+
+
+# --------------------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("bounds", [[0, 13], [0, 5, 13], [0, 1, 2, 7, 13], [0, 13, 13, 13], [0, 4, 4, 9, 13]])
+def test_lse_combine_reassembles_split_softmax(bounds):
+    """Softmax over a union of disjoint key ranges equals the lse-weighted merge
+    of per-range results; empty ranges (lse = -inf) get weight 0."""
+    q, k, v, R = _case(B=2, Sq=4, Skv=13, Hq=4, Hkv=2, d=6, E=5, seed=9)
+    for window in (0, 3):
+        o, l = attention(q, k, v, R, window=window, log_scale_base=32.0)
+        parts = [attention_partial(q, k, v, R, key_lo=a, key_hi=b, window=window, log_scale_base=32.0)
+                 for a, b in zip(bounds[:-1], bounds[1:])]
+        op = np.stack([p[0] for p in parts])                      # [S, B, Sq, Hq, d]
+        lp = np.stack([p[1].transpose(0, 2, 1) for p in parts])   # [S, B, Sq, Hq]
+        oc, lc = lse_combine(op, lp)
+        assert np.max(np.abs(oc - o)) <= 1e-12
+        assert np.max(np.abs(lc - l.transpose(0, 2, 1))) <= 1e-12
+
+
+def test_lse_combine_all_empty_rows():
+    op = np.zeros((3, 2, 4))
+    lp = np.full((3, 2), -np.inf)
+    o, l = lse_combine(op, lp)
+    assert np.all(o == 0.0) and np.all(np.isneginf(l))
