@@ -1,0 +1,202 @@
+"""Benchmark of the relative-position-bias attention hot path on one MI355X.
+
+A step is one pass of the prefill hot path over the sliding-window prefill
+workload (B=1, S=8192, Hq=64, Hkv=8, d=128, r_dim=64, E=512, window 4096,
+bf16): the relative-logit projection R = r.P followed by the attention
+prefill, with all inputs resident in HBM.  `value` is attention TFLOP/s
+(4*d*Hq flops per visible query/key pair) over the whole step.  The same JSON
+line carries the kernel-level roofline of the dominant kernel (attention,
+timed with HIP events on the stream it runs on), the split-KV decode
+workloads' KV GB/s, and the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_events(fn, iters, torch):
+    """Average duration (ms) of fn() measured with HIP events on the current stream."""
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in evs:
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / iters
+
+
+def cpu_baseline(w, inp, budget_s=15.0):
+    """The fp64 oracle on a sample of query rows of the workload (all heads)."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(7)
+    rows_all = [(0, int(t)) for t in rng.permutation(w.Sq)]
+
+    def R_row(b, t):
+        return oracle.relproj(inp["r"][b, t], inp["P"])
+
+    done, flops, t_used = 0, 0.0, 0.0
+    batch = 8
+    while t_used < budget_s and done < len(rows_all):
+        rows = rows_all[done:done + batch]
+        t0 = time.perf_counter()
+        oracle.attention_rows(inp["q"], inp["k"], inp["v"], R_row, rows, window=w.window,
+                              log_scale_base=w.log_scale_base)
+        t_used += time.perf_counter() - t0
+        for _, t in rows:
+            p = w.Skv - w.Sq + t
+            lo = 0 if w.window == 0 else max(0, p - w.window + 1)
+            flops += 4.0 * w.d * w.Hq * (p - lo + 1)
+        done += len(rows)
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} query rows x {w.Hq} heads of {w.name} (fp64 NumPy, R rows recomputed "
+                      f"from r and P), {t_used:.1f} s"}
+
+
+def decode_leg(rba, torch, name, reps):
+    from workloads import CONFIGS, make_inputs
+    w = CONFIGS[name]
+    log(f"decode {name}: generating inputs")
+    inp = make_inputs(w)
+    d = {k: v.to("cuda") for k, v in inp.items()}
+    del inp
+    R = rba.relproj(d["r"], d["P"])
+    splits = rba.num_splits(d["q"], d["k"], d["v"], R, window=w.window)
+    o = torch.empty_like(d["q"])
+    need = rba.decode_workspace_bytes(d["q"], d["k"], d["v"], R, window=w.window, splits=splits)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+    def run():
+        rba.attn_decode(d["q"], d["k"], d["v"], R, window=w.window, log_scale_base=w.log_scale_base,
+                        num_splits=splits, out=o, workspace=ws)
+
+    for _ in range(3):
+        run()
+    ms = time_events(run, reps, torch)
+    gbs = w.kv_bytes() / (ms * 1e-3) / 1e9
+    res = {"ms": round(ms, 4), "kv_GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+           "num_splits": splits, "kv_bytes": w.kv_bytes()}
+    del d, R, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              f"(every box has one GPU and the path needs no collective).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import relative_position_bias_rba_amd as rba
+    from workloads import CONFIGS, make_inputs
+
+    w = CONFIGS["c2_swa_prefill"]
+    log(f"prefill workload {w}")
+    inp = make_inputs(w)
+    d = {k: v.to("cuda") for k, v in inp.items()}
+    R = torch.empty(w.B, w.Sq, w.Hq, w.E, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(d["q"])
+
+    def step():
+        Rn = rba.relproj(d["r"], d["P"])
+        rba.attn_prefill(d["q"], d["k"], d["v"], Rn, window=w.window, log_scale_base=w.log_scale_base, out=o)
+        return Rn
+
+    for _ in range(args.warmup):
+        R = step()
+    torch.cuda.synchronize()
+
+    # whole-step timing
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        R = step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # kernel-level timing with HIP events on the stream the kernels run on
+    ms_attn = time_events(lambda: rba.attn_prefill(d["q"], d["k"], d["v"], R, window=w.window,
+                                                   log_scale_base=w.log_scale_base, out=o),
+                          max(args.steps, 10), torch)
+    ms_relproj = time_events(lambda: rba.relproj(d["r"], d["P"]), max(args.steps, 10), torch)
+
+    flops = w.attn_flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = flops / (ms_attn * 1e-3) / 1e12
+    relproj_bytes = w.B * w.Sq * w.Hq * w.E * 2 + w.B * w.Sq * w.r_dim * 2 + w.Hq * w.r_dim * w.E * 2
+    out = {
+        "metric": "rel-bias attn prefill TFLOP/s & decode KV GB/s (% of MI355X roofline)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normals)",
+        "config": {"workload": "sliding-window prefill B=1 S=8192 Hq=64 Hkv=8 d=128 r_dim=64 E=512 W=4096 "
+                               "(relproj + attention per step)",
+                   "global_batch": w.B, "seq_len": w.Sq, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_fwd_kernel<bf16, 2>", "avg_ms": round(ms_attn, 4),
+                     "algorithmic_flops": flops},
+        "kernels": {"attn_prefill_ms": round(ms_attn, 4), "attn_prefill_tflops": round(attn_tflops, 2),
+                    "relproj_ms": round(ms_relproj, 4),
+                    "relproj_GBps": round(relproj_bytes / (ms_relproj * 1e-3) / 1e9, 1),
+                    "relproj_frac_hbm": round(relproj_bytes / (ms_relproj * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+    del R, o
+    d_cpu = inp
+    del d
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        out["decode"] = {}
+        for name in ("c4_decode_swa", "c4_decode_full", "c5_long_decode"):
+            out["decode"][name] = decode_leg(rba, torch, name, 20)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(w, d_cpu, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,137 @@
+/*
+ * rba.h - C ABI of librba: causal grouped-query attention (head dim 128) with a
+ * learned, query-conditioned relative-position bias, for AMD MI355X (gfx950).
+ *
+ * What is computed (sources are web pages, cited by title and section):
+ *   [S-RPB]  "SGLang と Miles が Inkling を初日からサポート" (winzheng.jp), section
+ *            "相対位置バイアス付き Attention": each token carries a relative
+ *            feature r next to q, k, v; a learned matrix P per head maps r to
+ *            relative logits indexed by causal distance; the logit of query i,
+ *            key j, head h is the scaled dot product plus the entry for i-j;
+ *            distances past the extent add nothing; future keys are masked;
+ *            layers are sliding-window or full, and full layers may scale the
+ *            logits by a length-dependent log factor.
+ *   [V-ARCH] "vLLM TML Inkling サポート" (agentlenshq.com), section
+ *            "TML Inkling モデルアーキテクチャ": every layer is GQA with head
+ *            size 128; the relative term is added before softmax.
+ *   [V-OPT]  same page, section "低レイテンシコレクティブとカーネル": the
+ *            split-KV factor (num_splits) is chosen per batch size and KV length.
+ *
+ * For batch b, query head h (kv head g = h / (Hq/Hkv)), query row t at
+ * position p = Skv - Sq + t, and key j:
+ *     visible(p, j) = j <= p  and  (window == 0  or  p - j < window)
+ *     f(p)          = log_scale_base > 0 ? ln(p + 1) / ln(log_scale_base) : 1
+ *     s(t, j)       = f(p) * ( scale * <q[b,t,h,:], k[b,j,g,:]> + bias )
+ *     bias          = (R != NULL and p - j < E) ? R[b,t,h,p-j] : 0
+ *     o[b,t,h,:]    = sum_j softmax_j(s(t, .))[j] * v[b,j,g,:]   (visible j only)
+ *     lse[b,h,t]    = ln sum_j exp(s(t, j))                        (natural log)
+ * and R itself comes from rba_relproj:  R[b,t,h,e] = sum_c r[b,t,c] * P[h,c,e].
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; all work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and runs asynchronously.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is launched and outputs are left untouched.  No C++
+ *     exception crosses this boundary.
+ *   - Strides are in ELEMENTS.  The innermost dimension (d, or E for R) must be
+ *     contiguous.  Base pointers must be 16-byte aligned and the b/s/h strides
+ *     of q, k, v and o multiples of 16 bytes.
+ *   - dtype RBA_BF16: bf16 inputs, fp32 accumulation and softmax, bf16 output,
+ *     fp32 lse.  RBA_FP32: fp32 everywhere.
+ */
+#ifndef RBA_H
+#define RBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rba_status {
+    RBA_OK = 0,
+    RBA_E_INVALID = 1,     /* null pointer, bad shape/stride/alignment, Sq > Skv, window < 0 ... */
+    RBA_E_UNSUPPORTED = 2, /* valid but not built: d != 128, dtype combination, r_dim > 128, G > 256 */
+    RBA_E_WORKSPACE = 3,   /* decode workspace missing or smaller than rba_decode_workspace_bytes */
+    RBA_E_LAUNCH = 4       /* the HIP runtime reported an error when enqueueing a kernel */
+} rba_status;
+
+typedef enum rba_dtype {
+    RBA_FP32 = 0,
+    RBA_BF16 = 1
+} rba_dtype;
+
+/* Shapes, pointers and options of one attention call (prefill or decode).
+ *   q, o : [B, Sq, Hq, d]    strides q_s / o_s = {b, s, h}
+ *   k, v : [B, Skv, Hkv, d]  strides k_s / v_s = {b, s, h}
+ *   R    : [B, Sq, Hq, E]    strides R_s = {b, t, h}; NULL = no bias (E ignored)
+ *   lse  : [B, Hq, Sq] fp32, contiguous; NULL = not written                     */
+typedef struct rba_attn_args {
+    rba_dtype dt;
+    int B, Sq, Skv, Hq, Hkv, d, E;
+    int window;            /* 0 = full causal; > 0: key visible iff 0 <= p - j < window */
+    float scale;           /* multiplies q.k only, usually 1/sqrt(d) */
+    float log_scale_base;  /* 0 = off; > 1: logits multiplied by ln(p+1)/ln(base) */
+    const void *q, *k, *v;
+    const void *R;
+    void *o;
+    float *lse;
+    int64_t q_s[3], k_s[3], v_s[3], o_s[3], R_s[3];
+} rba_attn_args;
+
+/* R = r . P per head  ([S-RPB], the relative-logit projection).
+ *   r : [T, r_dim] (in_dt), row stride r_stride_t elements, channel contiguous
+ *   P : [Hq, r_dim, E] (in_dt), contiguous
+ *   R : [T, Hq, E] (out_dt), contiguous
+ * in_dt/out_dt may each be RBA_BF16 or RBA_FP32 (fp32 accumulation always;
+ * bf16 output is rounded to nearest even).  1 <= r_dim <= 128, E >= 1.
+ * T = 0 is a no-op.                                                          */
+rba_status rba_relproj(rba_dtype in_dt, rba_dtype out_dt, int64_t T, int Hq, int r_dim, int E,
+                       const void *r, int64_t r_stride_t, const void *P, void *R, void *stream);
+
+/* Attention over all keys for every query row ([S-RPB], [V-ARCH]); one pass,
+ * no workspace.  Any 1 <= Sq <= Skv is accepted (rows bottom-right aligned);
+ * Sq = 0 is a no-op.                                                         */
+rba_status rba_attn_prefill(const rba_attn_args *args, void *stream);
+
+/* Split-KV count the library picks for `args` on a device with `num_cus`
+ * compute units ([V-OPT]: from batch, kv heads and KV length).  num_cus <= 0
+ * queries the current device.  Returns >= 1, or 0 if args is invalid.      */
+int rba_num_splits(const rba_attn_args *args, int num_cus);
+
+/* Bytes of workspace rba_attn_decode needs for `num_splits` splits
+ * (0 = the heuristic's choice on the current device).  0 when one split is
+ * used (no workspace needed).  Layout: fp32 partial outputs
+ * [splits][B][Sq][Hq][d] followed by fp32 partial lse [splits][B][Sq][Hq].  */
+size_t rba_decode_workspace_bytes(const rba_attn_args *args, int num_splits);
+
+/* Split-KV attention for a few query rows against a long cache: each split
+ * covers a contiguous range of key tiles and writes its normalised partial
+ * output and lse into `workspace`; rba_splitkv_combine then merges them on
+ * the same stream.  num_splits = 0 uses rba_num_splits; 1 writes o directly.
+ * Returns RBA_E_WORKSPACE if workspace is NULL or too small when needed.   */
+rba_status rba_attn_decode(const rba_attn_args *args, int num_splits, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Merge split partials into args->o (and args->lse if non-NULL):
+ *   M = max_s lse_s;  w_s = exp(lse_s - M);  o = sum_s w_s o_s / sum_s w_s;
+ *   lse = M + ln sum_s w_s.  Splits with lse = -inf get weight 0; a row whose
+ *   splits are all empty gets o = 0, lse = -inf.
+ *   o_part : [num_splits][B][Sq][Hq][d] fp32 contiguous
+ *   lse_part : [num_splits][B][Sq][Hq] fp32 contiguous                      */
+rba_status rba_splitkv_combine(const float *o_part, const float *lse_part, int num_splits,
+                               const rba_attn_args *args, void *stream);
+
+/* Static description of a status code. */
+const char *rba_status_string(rba_status status);
+
+/* Version of the library as an integer (major*10000 + minor*100 + patch). */
+int rba_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RBA_H */

@@ -1,0 +1,212 @@
+"""Python binding of librba: relative-position-bias attention on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the gfx950
+kernels of ``librba.so`` (built in-tree by ``relative_position_bias_rba_amd.build``);
+torch provides device memory and the current HIP stream.  Importing this
+package fails loudly if the library has not been built.
+
+Layouts (head dim contiguous):
+  q, o [B, Sq, Hq, 128]   k, v [B, Skv, Hkv, 128]   r [B, Sq, r_dim]
+  P [Hq, r_dim, E]        R [B, Sq, Hq, E]          lse [B, Hq, Sq]
+Query row t sits at position Skv - Sq + t.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "relproj", "attn_prefill", "attn_decode", "splitkv_combine", "num_splits",
+    "decode_workspace_bytes", "lib_path", "RBAError",
+    "RBA_OK", "RBA_E_INVALID", "RBA_E_UNSUPPORTED", "RBA_E_WORKSPACE", "RBA_E_LAUNCH",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "librba.so")
+
+RBA_OK, RBA_E_INVALID, RBA_E_UNSUPPORTED, RBA_E_WORKSPACE, RBA_E_LAUNCH = range(5)
+RBA_FP32, RBA_BF16 = 0, 1
+
+
+class RBAError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn}: {_lib.rba_status_string(code).decode()} (status {code})")
+
+
+class _AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("dt", ctypes.c_int),
+        ("B", ctypes.c_int), ("Sq", ctypes.c_int), ("Skv", ctypes.c_int),
+        ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("d", ctypes.c_int), ("E", ctypes.c_int),
+        ("window", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("log_scale_base", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("R", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("q_s", ctypes.c_int64 * 3), ("k_s", ctypes.c_int64 * 3), ("v_s", ctypes.c_int64 * 3),
+        ("o_s", ctypes.c_int64 * 3), ("R_s", ctypes.c_int64 * 3),
+    ]
+
+
+def _load():
+    if not os.path.exists(lib_path):
+        raise ImportError(
+            f"librba.so not found at {lib_path}; build it with "
+            "`python -m relative_position_bias_rba_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(lib_path)
+    P = ctypes.POINTER(_AttnArgs)
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.rba_relproj.argtypes = [ci, ci, i64, ci, ci, ci, vp, i64, vp, vp, vp]
+    lib.rba_relproj.restype = ci
+    lib.rba_attn_prefill.argtypes = [P, vp]
+    lib.rba_attn_prefill.restype = ci
+    lib.rba_num_splits.argtypes = [P, ci]
+    lib.rba_num_splits.restype = ci
+    lib.rba_decode_workspace_bytes.argtypes = [P, ci]
+    lib.rba_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.rba_attn_decode.argtypes = [P, ci, vp, ctypes.c_size_t, vp]
+    lib.rba_attn_decode.restype = ci
+    lib.rba_splitkv_combine.argtypes = [vp, vp, ci, P, vp]
+    lib.rba_splitkv_combine.restype = ci
+    lib.rba_status_string.argtypes = [ci]
+    lib.rba_status_string.restype = ctypes.c_char_p
+    lib.rba_version.argtypes = []
+    lib.rba_version.restype = ci
+    return lib
+
+
+_lib = _load()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return RBA_BF16
+    if t.dtype == torch.float32:
+        return RBA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(fn: str, code: int):
+    if code != RBA_OK:
+        raise RBAError(fn, code)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def make_args(q, k, v, R=None, o=None, lse=None, *, window=0, scale=None, log_scale_base=0.0,
+              dt=None) -> _AttnArgs:
+    """Fill the C argument struct from tensors (shapes and strides only)."""
+    a = _AttnArgs()
+    B, Sq, Hq, d = q.shape
+    a.dt = _dt(q) if dt is None else dt
+    a.B, a.Sq, a.Skv, a.Hq, a.Hkv, a.d = B, Sq, k.shape[1], Hq, k.shape[2], d
+    a.E = 0 if R is None else R.shape[3]
+    a.window = int(window)
+    a.scale = float(1.0 / math.sqrt(d) if scale is None else scale)
+    a.log_scale_base = float(log_scale_base or 0.0)
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.R = None if R is None else R.data_ptr()
+    a.o = None if o is None else o.data_ptr()
+    a.lse = None if lse is None else lse.data_ptr()
+    for name, t in (("q_s", q), ("k_s", k), ("v_s", v), ("o_s", o), ("R_s", R)):
+        if t is not None:
+            if t.stride(3) != 1:
+                raise ValueError(f"{name[0]}: innermost dimension must be contiguous")
+            getattr(a, name)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    return a
+
+
+def _check_attn_inputs(q, k, v, R):
+    for t in (q, k, v) + (() if R is None else (R,)):
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+    if k.dtype != q.dtype or v.dtype != q.dtype or (R is not None and R.dtype != q.dtype):
+        raise TypeError("q, k, v and R must share one dtype")
+
+
+def relproj(r: torch.Tensor, P: torch.Tensor, out_dtype=None) -> torch.Tensor:
+    """R[..., h, e] = sum_c r[..., c] P[h, c, e] on the GPU (MFMA kernel)."""
+    if not (r.is_cuda and P.is_cuda):
+        raise ValueError("tensors must live on the GPU")
+    Hq, r_dim, E = P.shape
+    if r.shape[-1] != r_dim:
+        raise ValueError("r_dim mismatch")
+    P = P.contiguous()
+    r2 = r.reshape(-1, r_dim)
+    if r2.stride(1) != 1:
+        r2 = r2.contiguous()
+    out_dtype = r.dtype if out_dtype is None else out_dtype
+    R = torch.empty(*r.shape[:-1], Hq, E, dtype=out_dtype, device=r.device)
+    code = _lib.rba_relproj(_dt(r), _dt(R), r2.shape[0], Hq, r_dim, E, _ptr(r2), r2.stride(0),
+                            _ptr(P), _ptr(R), _stream(r.device))
+    _check("rba_relproj", code)
+    return R
+
+
+def attn_prefill(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0, return_lse=False,
+                 out=None):
+    """Attention of every query row over its visible keys (one pass)."""
+    _check_attn_inputs(q, k, v, R)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    lse = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=q.device) \
+        if return_lse else None
+    a = make_args(q, k, v, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base)
+    _check("rba_attn_prefill", _lib.rba_attn_prefill(ctypes.byref(a), _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
+def num_splits(q, k, v, R=None, *, window=0, num_cus=0, log_scale_base=0.0) -> int:
+    a = make_args(q, k, v, R, q, None, window=window, log_scale_base=log_scale_base)
+    return _lib.rba_num_splits(ctypes.byref(a), int(num_cus))
+
+
+def decode_workspace_bytes(q, k, v, R=None, *, window=0, splits=0) -> int:
+    a = make_args(q, k, v, R, q, None, window=window)
+    return _lib.rba_decode_workspace_bytes(ctypes.byref(a), int(splits))
+
+
+def attn_decode(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0, num_splits=0,
+                return_lse=False, out=None, workspace=None):
+    """Split-KV attention of a few query rows against a long KV cache."""
+    _check_attn_inputs(q, k, v, R)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    lse = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=q.device) \
+        if return_lse else None
+    a = make_args(q, k, v, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base)
+    splits = int(num_splits)
+    if splits == 0:
+        splits = _lib.rba_num_splits(ctypes.byref(a), 0)
+        if splits <= 0:
+            _check("rba_num_splits", RBA_E_INVALID)
+    need = _lib.rba_decode_workspace_bytes(ctypes.byref(a), splits)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = _lib.rba_attn_decode(ctypes.byref(a), splits, ws_ptr, ws_bytes, _stream(q.device))
+    _check("rba_attn_decode", code)
+    return (o, lse) if return_lse else o
+
+
+def splitkv_combine(o_part, lse_part, q_like, k_like, *, out=None, return_lse=False):
+    """Merge split partials o_part [S, B, Sq, Hq, d] / lse_part [S, B, Sq, Hq] (fp32)."""
+    S, B, Sq, Hq, d = o_part.shape
+    o = torch.empty(B, Sq, Hq, d, dtype=q_like.dtype, device=o_part.device) if out is None else out
+    lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=o_part.device) if return_lse else None
+    a = make_args(q_like, k_like, k_like, None, o, lse)
+    code = _lib.rba_splitkv_combine(ctypes.c_void_p(o_part.data_ptr()), ctypes.c_void_p(lse_part.data_ptr()),
+                                    S, ctypes.byref(a), _stream(o_part.device))
+    _check("rba_splitkv_combine", code)
+    return (o, lse) if return_lse else o

@@ -1,0 +1,239 @@
+// C ABI of librba: argument validation, work planning (query-block size,
+// split-KV count) and kernel dispatch.  Declarations and the meaning of every
+// argument are in include/rba.h.
+#include "rba.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "rba_internal.h"
+
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxSplits = 1024;
+constexpr int kMinTilesPerSplit = 4;
+
+int elem_size(rba_dtype dt) { return dt == RBA_BF16 ? 2 : 4; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool strides_ok(const int64_t s[3], int64_t mult) {
+    for (int i = 0; i < 3; ++i)
+        if (s[i] < 0 || s[i] % mult != 0) return false;
+    return true;
+}
+
+rba_status validate_attn(const rba_attn_args *a) {
+    if (a == nullptr) return RBA_E_INVALID;
+    if (a->dt != RBA_BF16 && a->dt != RBA_FP32) return RBA_E_UNSUPPORTED;
+    if (a->d <= 0) return RBA_E_INVALID;
+    if (a->d != kHeadDim) return RBA_E_UNSUPPORTED;
+    if (a->B < 0 || a->Sq < 0 || a->Skv < 0 || a->Hq < 1 || a->Hkv < 1) return RBA_E_INVALID;
+    if (a->Hq % a->Hkv != 0) return RBA_E_INVALID;
+    if (a->Sq > a->Skv) return RBA_E_INVALID;
+    if (a->window < 0) return RBA_E_INVALID;
+    if (!isfinite(a->scale)) return RBA_E_INVALID;
+    if (!(a->log_scale_base == 0.f || (isfinite(a->log_scale_base) && a->log_scale_base > 1.f)))
+        return RBA_E_INVALID;
+    if (a->R != nullptr && a->E < 1) return RBA_E_INVALID;
+    const int G = a->Hq / a->Hkv;
+    const int maxc = rba::attn_max_columns(a->dt == RBA_FP32 ? rba::AttnVariant::FP32 : rba::AttnVariant::BF16_WIDE);
+    if (G > maxc) return RBA_E_UNSUPPORTED;
+    if ((int64_t)a->B * a->Sq == 0) return RBA_OK;  // nothing to do, pointers unused
+    if (a->q == nullptr || a->k == nullptr || a->v == nullptr || a->o == nullptr) return RBA_E_INVALID;
+    if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->o, 16)) return RBA_E_INVALID;
+    const int64_t ch = 16 / elem_size(a->dt);
+    if (!strides_ok(a->q_s, ch) || !strides_ok(a->k_s, ch) || !strides_ok(a->v_s, ch) || !strides_ok(a->o_s, ch))
+        return RBA_E_INVALID;
+    if (a->R != nullptr) {
+        if (!aligned(a->R, elem_size(a->dt))) return RBA_E_INVALID;
+        if (!strides_ok(a->R_s, 1)) return RBA_E_INVALID;
+    }
+    if (a->lse != nullptr && !aligned(a->lse, 4)) return RBA_E_INVALID;
+    return RBA_OK;
+}
+
+struct Plan {
+    rba::AttnVariant var;
+    int QB, nqb, N;
+};
+
+// Query-block size: all G heads of a kv head share a workgroup, so G*QB
+// columns must fit the variant; QB <= 32 keeps the staged bias slab small.
+Plan make_plan(const rba_attn_args *a) {
+    Plan pl;
+    const int G = a->Hq / a->Hkv;
+    const int rows = std::max(1, std::min(a->Sq, 32));
+    if (a->dt == RBA_FP32)
+        pl.var = rba::AttnVariant::FP32;
+    else if (G * rows > 128)
+        pl.var = rba::AttnVariant::BF16_WIDE;   // two 32-column tiles per wave
+    else
+        pl.var = rba::AttnVariant::BF16_NARROW;
+    const int maxc = rba::attn_max_columns(pl.var);
+    pl.QB = std::max(1, std::min(rows, maxc / G));
+    pl.nqb = a->Sq > 0 ? (a->Sq + pl.QB - 1) / pl.QB : 0;
+    pl.N = a->dt == RBA_FP32 ? 32 : 64;
+    return pl;
+}
+
+int tiles_last_block(const rba_attn_args *a, const Plan &pl) {
+    if (a->Sq == 0) return 0;
+    const int p_max = a->Skv - 1;
+    const int p_min = a->Skv - a->Sq + (pl.nqb - 1) * pl.QB;
+    const int lo = a->window > 0 ? std::max(0, p_min - a->window + 1) : 0;
+    return p_max / pl.N - lo / pl.N + 1;
+}
+
+int heuristic_splits(const rba_attn_args *a, const Plan &pl, int num_cus) {
+    const int64_t base = (int64_t)a->B * a->Hkv * pl.nqb;
+    if (base <= 0) return 1;
+    const int64_t target = 2 * (int64_t)num_cus;  // work items to keep every CU busy
+    int64_t s = (target + base - 1) / base;
+    const int n_t = tiles_last_block(a, pl);
+    s = std::min<int64_t>(s, std::max(1, n_t / kMinTilesPerSplit));
+    s = std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplits));
+    return (int)s;
+}
+
+int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
+
+rba::AttnParams make_params(const rba_attn_args *a, const Plan &pl, int splits) {
+    rba::AttnParams p{};
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.R = a->R;
+    p.o = a->o;
+    p.lse = a->lse;
+    p.qs0 = a->q_s[0], p.qs1 = a->q_s[1], p.qs2 = a->q_s[2];
+    p.ks0 = a->k_s[0], p.ks1 = a->k_s[1], p.ks2 = a->k_s[2];
+    p.vs0 = a->v_s[0], p.vs1 = a->v_s[1], p.vs2 = a->v_s[2];
+    p.os0 = a->o_s[0], p.os1 = a->o_s[1], p.os2 = a->o_s[2];
+    p.Rs0 = a->R_s[0], p.Rs1 = a->R_s[1], p.Rs2 = a->R_s[2];
+    p.B = a->B, p.Sq = a->Sq, p.Skv = a->Skv, p.Hq = a->Hq, p.Hkv = a->Hkv;
+    p.G = a->Hq / a->Hkv;
+    p.E = a->R != nullptr ? a->E : 0;
+    p.window = a->window;
+    p.scale_log2e = a->scale * 1.4426950408889634f;
+    p.inv_ln_base = a->log_scale_base > 0.f ? (float)(1.0 / log((double)a->log_scale_base)) : 0.f;
+    p.QB = pl.QB;
+    p.nqb = pl.nqb;
+    p.splits = splits;
+    const int64_t ch = 16 / elem_size(a->dt);
+    p.r_vec = a->R != nullptr && aligned(a->R, 16) && a->E % ch == 0 && a->R_s[0] % ch == 0 &&
+              a->R_s[1] % ch == 0 && a->R_s[2] % ch == 0;
+    return p;
+}
+
+size_t workspace_bytes(const rba_attn_args *a, int splits) {
+    if (splits <= 1) return 0;
+    const size_t rows = (size_t)a->B * a->Sq * a->Hq;
+    return (size_t)splits * rows * (kHeadDim + 1) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+rba_status rba_relproj(rba_dtype in_dt, rba_dtype out_dt, int64_t T, int Hq, int r_dim, int E, const void *r,
+                       int64_t r_stride_t, const void *P, void *R, void *stream) {
+    if ((in_dt != RBA_BF16 && in_dt != RBA_FP32) || (out_dt != RBA_BF16 && out_dt != RBA_FP32))
+        return RBA_E_UNSUPPORTED;
+    if (T < 0 || Hq < 1 || r_dim < 1 || E < 1) return RBA_E_INVALID;
+    if (r_dim > 128 || Hq > 65535) return RBA_E_UNSUPPORTED;
+    if (T == 0) return RBA_OK;
+    if (r == nullptr || P == nullptr || R == nullptr) return RBA_E_INVALID;
+    if (!aligned(r, 16) || !aligned(P, 16) || !aligned(R, 16)) return RBA_E_INVALID;
+    if (r_stride_t < r_dim) return RBA_E_INVALID;
+    const hipError_t e = rba::launch_relproj(in_dt == RBA_BF16, out_dt == RBA_BF16, T, Hq, r_dim, E, r, r_stride_t,
+                                             P, R, (hipStream_t)stream);
+    return e == hipSuccess ? RBA_OK : RBA_E_LAUNCH;
+}
+
+rba_status rba_attn_prefill(const rba_attn_args *args, void *stream) {
+    const rba_status st = validate_attn(args);
+    if (st != RBA_OK) return st;
+    if ((int64_t)args->B * args->Sq == 0) return RBA_OK;
+    const Plan pl = make_plan(args);
+    const rba::AttnParams p = make_params(args, pl, 1);
+    return rba::launch_attention(p, pl.var, (hipStream_t)stream) == hipSuccess ? RBA_OK : RBA_E_LAUNCH;
+}
+
+int rba_num_splits(const rba_attn_args *args, int num_cus) {
+    if (validate_attn(args) != RBA_OK) return 0;
+    if (num_cus <= 0) num_cus = device_cus();
+    if (num_cus <= 0) return 0;
+    const Plan pl = make_plan(args);
+    return heuristic_splits(args, pl, num_cus);
+}
+
+size_t rba_decode_workspace_bytes(const rba_attn_args *args, int num_splits) {
+    if (validate_attn(args) != RBA_OK || num_splits < 0 || num_splits > kMaxSplits) return 0;
+    if (num_splits == 0) num_splits = rba_num_splits(args, 0);
+    return workspace_bytes(args, num_splits);
+}
+
+rba_status rba_attn_decode(const rba_attn_args *args, int num_splits, void *workspace, size_t workspace_bytes_,
+                           void *stream) {
+    const rba_status st = validate_attn(args);
+    if (st != RBA_OK) return st;
+    if (num_splits < 0 || num_splits > kMaxSplits) return RBA_E_INVALID;
+    if ((int64_t)args->B * args->Sq == 0) return RBA_OK;
+    const Plan pl = make_plan(args);
+    if (num_splits == 0) {
+        const int cus = device_cus();
+        if (cus <= 0) return RBA_E_LAUNCH;
+        num_splits = heuristic_splits(args, pl, cus);
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (num_splits == 1) {
+        const rba::AttnParams p = make_params(args, pl, 1);
+        return rba::launch_attention(p, pl.var, s) == hipSuccess ? RBA_OK : RBA_E_LAUNCH;
+    }
+    const size_t need = workspace_bytes(args, num_splits);
+    if (workspace == nullptr || workspace_bytes_ < need || !aligned(workspace, 16)) return RBA_E_WORKSPACE;
+    rba::AttnParams p = make_params(args, pl, num_splits);
+    const size_t rows = (size_t)args->B * args->Sq * args->Hq;
+    p.o_part = (float *)workspace;
+    p.lse_part = p.o_part + (size_t)num_splits * rows * kHeadDim;
+    if (rba::launch_attention(p, pl.var, s) != hipSuccess) return RBA_E_LAUNCH;
+    return rba_splitkv_combine(p.o_part, p.lse_part, num_splits, args, stream);
+}
+
+rba_status rba_splitkv_combine(const float *o_part, const float *lse_part, int num_splits,
+                               const rba_attn_args *args, void *stream) {
+    const rba_status st = validate_attn(args);
+    if (st != RBA_OK) return st;
+    if (num_splits < 1 || num_splits > kMaxSplits) return RBA_E_INVALID;
+    if ((int64_t)args->B * args->Sq == 0) return RBA_OK;
+    if (o_part == nullptr || lse_part == nullptr || !aligned(o_part, 16) || !aligned(lse_part, 4))
+        return RBA_E_INVALID;
+    const hipError_t e =
+        rba::launch_combine(o_part, lse_part, num_splits, args->B, args->Sq, args->Hq, args->o, args->dt == RBA_BF16,
+                            args->o_s[0], args->o_s[1], args->o_s[2], args->lse, (hipStream_t)stream);
+    return e == hipSuccess ? RBA_OK : RBA_E_LAUNCH;
+}
+
+const char *rba_status_string(rba_status status) {
+    switch (status) {
+        case RBA_OK: return "ok";
+        case RBA_E_INVALID: return "invalid argument";
+        case RBA_E_UNSUPPORTED: return "unsupported shape or dtype";
+        case RBA_E_WORKSPACE: return "workspace missing or too small";
+        case RBA_E_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int rba_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Internal launch interface between the C ABI (rba_abi.cpp) and the gfx950
+// kernels (attn_kernels.hip, relproj_kernels.hip).  Host-side only types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rba {
+
+// One attention launch.  Query rows are grouped into blocks of QB consecutive
+// rows; a workgroup owns one (batch, kv head, query block, split) and all G
+// query heads of that kv head, so every K/V tile it stages serves G*QB
+// query columns.
+struct AttnParams {
+    const void *q, *k, *v, *R;
+    void *o;
+    float *lse;
+    float *o_part, *lse_part;  // split partials (splits > 1), else null
+    int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2, Rs0, Rs1, Rs2;
+    int B, Sq, Skv, Hq, Hkv, G, E, window;
+    float scale_log2e;   // scale * log2(e): the dot-product multiplier in the exp2 domain
+    float inv_ln_base;   // 1/ln(base) for the log-scale factor, 0 = off
+    int QB;              // query rows per block
+    int nqb;             // query blocks per (batch, kv head)
+    int splits;          // key-range splits per block
+    int r_vec;           // R rows allow 16-byte chunk loads
+};
+
+// Kernel variants.  WIDE: two 32-column tiles per wave (prefill, bf16).
+enum class AttnVariant { BF16_WIDE, BF16_NARROW, FP32 };
+
+// Largest G*QB one workgroup of the variant covers.
+int attn_max_columns(AttnVariant v);
+
+hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stream);
+
+hipError_t launch_combine(const float *o_part, const float *lse_part, int splits, int B, int Sq, int Hq,
+                          void *o, bool o_bf16, int64_t os0, int64_t os1, int64_t os2, float *lse,
+                          hipStream_t stream);
+
+hipError_t launch_relproj(bool in_bf16, bool out_bf16, int64_t T, int Hq, int r_dim, int E, const void *r,
+                          int64_t r_stride, const void *P, void *R, hipStream_t stream);
+
+}  // namespace rba

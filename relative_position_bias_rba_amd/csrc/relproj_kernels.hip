@@ -1,0 +1,216 @@
+// Relative-logit projection R[t, h, :] = r[t, :] . P[h]  for gfx950.
+//
+// Each token's relative feature r is mapped by a learned per-head matrix P to
+// a row of relative logits indexed by causal distance ("SGLang と Miles が
+// Inkling を初日からサポート", sections "Inkling のモデルアーキテクチャ" and
+// "相対位置バイアス付き Attention").
+//
+// The contraction is short (r_dim <= 128) and the output is E entries per
+// (token, head), so the kernel is bound by writing R.  A workgroup owns one
+// head and 256 tokens; it stages P[h]^T in LDS in chunks of 128 distances and
+// computes R^T tiles (32 distances x 32 tokens) with MFMA, A = P^T from LDS and
+// B = r^T from registers.  The A-operand row order makes every lane hold 16
+// consecutive distances of one token, so R is written with 16-byte stores.
+#include "rba_internal.h"
+
+#include <type_traits>
+
+namespace rba {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int NT = 256;
+constexpr int EC = 128;       // distances per LDS chunk
+constexpr int TPW = 64;       // tokens per wave (two 32-column tiles)
+constexpr int TPB = 4 * TPW;  // tokens per workgroup
+constexpr int KMAX = 128;     // largest r_dim
+
+__device__ __forceinline__ int mfma_row_key(int i) { return ((i >> 2) & 1) * 16 + (i >> 3) * 4 + (i & 3); }
+__device__ __forceinline__ int lds_row(int j) { return j ^ (((j >> 4) & 1) * 12); }
+
+template <typename TI, typename TO>
+__global__ __launch_bounds__(NT) void relproj_kernel(const TI *__restrict__ r, int64_t rs, const TI *__restrict__ P,
+                                                     TO *__restrict__ R, int64_t T, int Hq, int r_dim, int E) {
+    constexpr bool BF = sizeof(TI) == 2;
+    constexpr int PAD = BF ? 8 : 4;
+    // P^T chunk in LDS: EC rows (distances) x KP (+pad) channels
+    __shared__ __attribute__((aligned(16))) TI sP[EC * (KMAX + PAD)];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, lc = lane & 31;
+    const int h = blockIdx.y;
+    const int64_t tbase = (int64_t)blockIdx.x * TPB + wave * TPW;
+    const int KP = (r_dim + 15) & ~15;     // channels padded to a 16-multiple
+    const int PS = KP + PAD;               // LDS row stride
+    const bool r_vec = (r_dim % 8 == 0) && (rs % 8 == 0);
+    const bool e_vec = (E % (16 / (int)sizeof(TO))) == 0;
+
+    // B operands: r^T for this lane's token columns.
+    constexpr int KSTEP = BF ? 16 : 2;
+    constexpr int NKS = BF ? KMAX / 16 : KMAX / 2;
+    typedef typename std::conditional<BF, bf16x8, float>::type Frag;
+    Frag rf[2][BF ? 8 : 64];
+    const int nks = BF ? KP / 16 : KP / 2;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int64_t t = tbase + 32 * c + lc;
+        const bool ok = t < T;
+        const TI *rp = r + (ok ? t : 0) * rs;
+        if constexpr (BF) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                bf16x8 x = bf16x8{};
+                const int c0 = 16 * k + 8 * hh;
+                if (ok && k < nks) {
+                    if (r_vec && c0 + 8 <= r_dim) {
+                        x = *(const bf16x8 *)(rp + c0);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) x[i] = c0 + i < r_dim ? rp[c0 + i] : (__bf16)0.f;
+                    }
+                }
+                rf[c][k] = x;
+            }
+        } else {
+            const int KH = KP / 2;  // channels per lane half
+#pragma unroll
+            for (int k = 0; k < 64; ++k) {
+                const int ch = KH * hh + k;
+                rf[c][k] = (ok && k < KH && ch < r_dim) ? rp[ch] : 0.f;
+            }
+        }
+    }
+    (void)NKS;
+    (void)KSTEP;
+
+    const int arow_key = mfma_row_key(lc);
+    for (int e0 = 0; e0 < E; e0 += EC) {
+        // ---- stage P[h][:, e0:e0+EC]^T: each unit = 4 channels x 8 distances
+        __syncthreads();
+        const int units = (KP / 4) * (EC / 8);
+        for (int u = tid; u < units; u += NT) {
+            const int cq = u / (EC / 8), eq = u - cq * (EC / 8);
+            TI v[4][8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 4 * cq + i;
+                const int e = e0 + 8 * eq;
+                const TI *src = P + ((int64_t)h * r_dim + c) * E + e;
+                if (c < r_dim && (E % 8 == 0) && e + 8 <= E) {
+                    if constexpr (BF) {
+                        *(u32x4 *)v[i] = *(const u32x4 *)src;
+                    } else {
+                        *(u32x4 *)&v[i][0] = *(const u32x4 *)src;
+                        *(u32x4 *)&v[i][4] = *(const u32x4 *)(src + 4);
+                    }
+                } else {
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) v[i][x] = (c < r_dim && e + x < E) ? src[x] : (TI)0.f;
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                TI w[4] = {v[0][x], v[1][x], v[2][x], v[3][x]};
+                const int er = 8 * eq + x;  // distance row inside the chunk
+                TI *dst = &sP[(32 * (er >> 5) + lds_row(er & 31)) * PS + 4 * cq];
+                if constexpr (BF)
+                    *(u32x2 *)dst = *(const u32x2 *)w;
+                else
+                    *(u32x4 *)dst = *(const u32x4 *)w;
+            }
+        }
+        __syncthreads();
+
+        // ---- 4 distance tiles of 32 per chunk
+#pragma unroll
+        for (int et = 0; et < EC / 32; ++et) {
+            if (e0 + 32 * et >= E) break;
+            f32x16 acc[2] = {f32x16{}, f32x16{}};
+            const TI *arow = &sP[(32 * et + lds_row(arow_key)) * PS];
+            if constexpr (BF) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    if (k < nks) {
+                        const bf16x8 a = *(const bf16x8 *)(arow + 16 * k + 8 * hh);
+                        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, rf[0][k], acc[0], 0, 0, 0);
+                        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, rf[1][k], acc[1], 0, 0, 0);
+                    }
+                }
+            } else {
+                const int KH = KP / 2;
+#pragma unroll
+                for (int k4 = 0; k4 < 16; ++k4) {
+                    if (4 * k4 < KH) {
+                        const f32x4 a = *(const f32x4 *)(arow + KH * hh + 4 * k4);
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[x], rf[0][4 * k4 + x], acc[0], 0, 0, 0);
+                            acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[x], rf[1][4 * k4 + x], acc[1], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+            // lane holds distances e0 + 32et + 16hh + 0..15 of token column lc
+            const int eb = e0 + 32 * et + 16 * hh;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int64_t t = tbase + 32 * c + lc;
+                if (t >= T) continue;
+                TO *dst = R + (t * Hq + h) * (int64_t)E + eb;
+                if (e_vec && eb + 16 <= E) {
+                    if constexpr (sizeof(TO) == 2) {
+                        bf16x8 w0, w1;
+#pragma unroll
+                        for (int x = 0; x < 8; ++x) {
+                            w0[x] = (__bf16)acc[c][x];
+                            w1[x] = (__bf16)acc[c][8 + x];
+                        }
+                        *(bf16x8 *)dst = w0;
+                        *(bf16x8 *)(dst + 8) = w1;
+                    } else {
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            f32x4 w;
+#pragma unroll
+                            for (int x = 0; x < 4; ++x) w[x] = acc[c][4 * q4 + x];
+                            *(f32x4 *)(dst + 4 * q4) = w;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int x = 0; x < 16; ++x)
+                        if (eb + x < E) dst[x] = (TO)acc[c][x];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_relproj(bool in_bf16, bool out_bf16, int64_t T, int Hq, int r_dim, int E, const void *r,
+                          int64_t r_stride, const void *P, void *R, hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    const int64_t gx = (T + TPB - 1) / TPB;
+    if (gx > 0x7fffffff || Hq > 65535) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)gx, (unsigned)Hq), block(NT);
+    if (in_bf16 && out_bf16)
+        hipLaunchKernelGGL((relproj_kernel<__bf16, __bf16>), grid, block, 0, stream, (const __bf16 *)r, r_stride,
+                           (const __bf16 *)P, (__bf16 *)R, T, Hq, r_dim, E);
+    else if (in_bf16)
+        hipLaunchKernelGGL((relproj_kernel<__bf16, float>), grid, block, 0, stream, (const __bf16 *)r, r_stride,
+                           (const __bf16 *)P, (float *)R, T, Hq, r_dim, E);
+    else if (out_bf16)
+        hipLaunchKernelGGL((relproj_kernel<float, __bf16>), grid, block, 0, stream, (const float *)r, r_stride,
+                           (const float *)P, (__bf16 *)R, T, Hq, r_dim, E);
+    else
+        hipLaunchKernelGGL((relproj_kernel<float, float>), grid, block, 0, stream, (const float *)r, r_stride,
+                           (const float *)P, (float *)R, T, Hq, r_dim, E);
+    return hipGetLastError();
+}
+
+}  // namespace rba

@@ -1,0 +1,179 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects invalid arguments with the documented status before touching the GPU.
+No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import relative_position_bias_rba_amd as rba
+from relative_position_bias_rba_amd import (RBA_E_INVALID, RBA_E_UNSUPPORTED, RBA_E_WORKSPACE, RBA_OK,
+                                            make_args)
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "rba.h")
+lib = rba._lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rba_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("rba_relproj", "rba_attn_prefill", "rba_attn_decode", "rba_splitkv_combine",
+                 "rba_num_splits", "rba_decode_workspace_bytes", "rba_status_string"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    raw = ctypes.CDLL(rba.lib_path)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings_and_version():
+    for code in range(5):
+        assert lib.rba_status_string(code)
+    assert lib.rba_status_string(RBA_OK) == b"ok"
+    assert lib.rba_version() >= 100
+
+
+def _tensors(B=1, Sq=9, Skv=64, Hq=8, Hkv=2, d=128, E=16, dtype=torch.bfloat16):
+    q = torch.zeros(B, Sq, Hq, d, dtype=dtype)
+    k = torch.zeros(B, Skv, Hkv, d, dtype=dtype)
+    v = torch.zeros(B, Skv, Hkv, d, dtype=dtype)
+    R = torch.zeros(B, Sq, Hq, E, dtype=dtype)
+    o = torch.zeros_like(q)
+    return q, k, v, R, o
+
+
+def _prefill(a):
+    return lib.rba_attn_prefill(ctypes.byref(a), None)
+
+
+def _decode(a, splits=4, ws=None, nbytes=0):
+    return lib.rba_attn_decode(ctypes.byref(a), splits, ws, nbytes, None)
+
+
+def test_validation_rejects_bad_shapes():
+    q, k, v, R, o = _tensors()
+    cases = []
+    a = make_args(q, k, v, R, o); a.d = 64; cases.append((a, RBA_E_UNSUPPORTED))
+    a = make_args(q, k, v, R, o); a.d = 0; cases.append((a, RBA_E_INVALID))
+    a = make_args(q, k, v, R, o); a.Hkv = 3; cases.append((a, RBA_E_INVALID))
+    a = make_args(q, k, v, R, o); a.Sq = 100; cases.append((a, RBA_E_INVALID))
+    a = make_args(q, k, v, R, o); a.window = -1; cases.append((a, RBA_E_INVALID))
+    a = make_args(q, k, v, R, o); a.E = 0; cases.append((a, RBA_E_INVALID))
+    a = make_args(q, k, v, R, o); a.log_scale_base = 0.5; cases.append((a, RBA_E_INVALID))
+    a = make_args(q, k, v, R, o); a.scale = float("nan"); cases.append((a, RBA_E_INVALID))
+    a = make_args(q, k, v, R, o); a.dt = 7; cases.append((a, RBA_E_UNSUPPORTED))
+    a = make_args(q, k, v, R, o); a.Hq = 512; a.Hkv = 1; cases.append((a, RBA_E_UNSUPPORTED))
+    a = make_args(q, k, v, R, o); a.B = -1; cases.append((a, RBA_E_INVALID))
+    for a, want in cases:
+        assert _prefill(a) == want
+        assert _decode(a) == want
+        assert lib.rba_num_splits(ctypes.byref(a), 256) == 0
+
+
+def test_validation_rejects_bad_pointers_and_strides():
+    q, k, v, R, o = _tensors()
+    a = make_args(q, k, v, R, o); a.q = None
+    assert _prefill(a) == RBA_E_INVALID
+    a = make_args(q, k, v, R, o); a.o = None
+    assert _prefill(a) == RBA_E_INVALID
+    a = make_args(q, k, v, R, o); a.k = k.data_ptr() + 2
+    assert _prefill(a) == RBA_E_INVALID
+    a = make_args(q, k, v, R, o); a.q_s[1] = 1028      # not a 16-byte multiple for bf16
+    assert _prefill(a) == RBA_E_INVALID
+    a = make_args(q, k, v, R, o); a.v_s[0] = -8
+    assert _prefill(a) == RBA_E_INVALID
+    a = make_args(q, k, v, R, o); a.R = R.data_ptr() + 1
+    assert _prefill(a) == RBA_E_INVALID
+    a = make_args(q, k, v, R, o); a.lse = o.data_ptr() + 2
+    assert _prefill(a) == RBA_E_INVALID
+    with pytest.raises(ValueError):
+        make_args(q.transpose(2, 3), k, v, R, o)
+
+
+def test_empty_inputs_are_noops():
+    q, k, v, R, o = _tensors(Sq=0)
+    a = make_args(q, k, v, R, o); a.q = None; a.o = None
+    assert _prefill(a) == RBA_OK
+    assert _decode(a, splits=3) == RBA_OK
+    q, k, v, R, o = _tensors(B=0)
+    a = make_args(q, k, v, R, o)
+    assert _prefill(a) == RBA_OK
+    r = torch.zeros(0, 64)
+    P = torch.zeros(4, 64, 16)
+    assert lib.rba_relproj(0, 0, 0, 4, 64, 16, None, 64, None, None, None) == RBA_OK
+
+
+def test_decode_workspace_checks():
+    q, k, v, R, o = _tensors(B=2, Sq=9, Skv=640, Hq=16, Hkv=2)
+    a = make_args(q, k, v, R, o)
+    need = lib.rba_decode_workspace_bytes(ctypes.byref(a), 4)
+    assert need == 4 * 2 * 9 * 16 * (128 + 1) * 4
+    assert lib.rba_decode_workspace_bytes(ctypes.byref(a), 1) == 0
+    assert _decode(a, splits=4, ws=None, nbytes=0) == RBA_E_WORKSPACE
+    buf = torch.zeros(need // 4, dtype=torch.float32)
+    assert _decode(a, splits=4, ws=ctypes.c_void_p(buf.data_ptr()), nbytes=need - 4) == RBA_E_WORKSPACE
+    assert _decode(a, splits=4, ws=ctypes.c_void_p(buf.data_ptr() + 4), nbytes=need) == RBA_E_WORKSPACE
+    assert _decode(a, splits=-1) == RBA_E_INVALID
+    assert _decode(a, splits=5000) == RBA_E_INVALID
+    assert lib.rba_splitkv_combine(None, None, 4, ctypes.byref(a), None) == RBA_E_INVALID
+    assert lib.rba_splitkv_combine(ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(buf.data_ptr()), 0,
+                                   ctypes.byref(a), None) == RBA_E_INVALID
+
+
+def test_relproj_validation():
+    r = torch.zeros(8, 64, dtype=torch.bfloat16)
+    P = torch.zeros(4, 64, 16, dtype=torch.bfloat16)
+    R = torch.zeros(8, 4, 16, dtype=torch.bfloat16)
+    pr, pP, pR = (ctypes.c_void_p(t.data_ptr()) for t in (r, P, R))
+    assert lib.rba_relproj(1, 1, 8, 4, 200, 16, pr, 200, pP, pR, None) == RBA_E_UNSUPPORTED
+    assert lib.rba_relproj(1, 1, 8, 4, 0, 16, pr, 64, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(1, 1, 8, 4, 64, 0, pr, 64, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(1, 1, -1, 4, 64, 16, pr, 64, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(1, 1, 8, 4, 64, 16, None, 64, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(1, 1, 8, 4, 64, 16, pr, 32, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(1, 1, 8, 4, 64, 16, ctypes.c_void_p(r.data_ptr() + 2), 64, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(3, 1, 8, 4, 64, 16, pr, 64, pP, pR, None) == RBA_E_UNSUPPORTED
+
+
+# --------------------------------------------------------------------------- split heuristic (host logic)
+
+def _split_args(B, Sq, Skv, Hq=64, Hkv=8, window=0):
+    q = torch.zeros(1, 1, 1, 1)
+    a = rba._AttnArgs()
+    a.dt, a.B, a.Sq, a.Skv, a.Hq, a.Hkv, a.d, a.E = 1, B, Sq, Skv, Hq, Hkv, 128, 512
+    a.window, a.scale, a.log_scale_base = window, 0.088, 0.0
+    fake = 1 << 20
+    a.q = a.k = a.v = a.o = a.R = fake
+    for name in ("q_s", "k_s", "v_s", "o_s", "R_s"):
+        getattr(a, name)[:] = [8, 8, 8]
+    return a
+
+
+@pytest.mark.parametrize("B,Sq,Skv,window", [(64, 9, 9216, 0), (64, 9, 9216, 4096), (1, 1, 262144, 0),
+                                              (1, 9, 300, 0), (4, 1, 64, 0), (1, 32, 100000, 4096)])
+def test_num_splits_heuristic_properties(B, Sq, Skv, window):
+    a = _split_args(B, Sq, Skv, window=window)
+    s = lib.rba_num_splits(ctypes.byref(a), 256)
+    assert 1 <= s <= 1024
+    # never more splits than 4-tile chunks of the visible key range of a block
+    lo = 0 if window == 0 else max(0, Skv - Sq - window + 1)
+    tiles = (Skv - 1) // 64 - lo // 64 + 1
+    assert s <= max(1, tiles // 4)
+    # more compute units never means fewer splits
+    assert lib.rba_num_splits(ctypes.byref(a), 512) >= s
+
+
+def test_num_splits_reference_points():
+    # 64 sequences x 8 kv heads already give two work items per CU: no split
+    assert lib.rba_num_splits(ctypes.byref(_split_args(64, 9, 9216)), 256) == 1
+    # one sequence, 8 kv heads, 256K keys: spread over the whole chip
+    assert lib.rba_num_splits(ctypes.byref(_split_args(1, 1, 262144)), 256) == 64

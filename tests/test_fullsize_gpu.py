@@ -1,0 +1,93 @@
+"""Full-size workloads on the GPU, in the launch configuration the benchmark
+times (prefill as one pass, decode with the library's split heuristic), checked
+on sampled query rows that the fp64 oracle computes one by one (R for those
+rows is recomputed by the oracle from r and P)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rows_for(w, n_random, seed):
+    g = np.random.default_rng(seed)
+    if w.Sq <= 32:
+        fixed = list(range(w.Sq))                 # decode: every new row
+    else:
+        fixed = [t for t in (0, 1, 511, 512, 4095, 4096, w.Sq - 1) if t < w.Sq]
+    rows = []
+    for b in range(w.B):
+        ts = set(fixed) | set(int(x) for x in g.integers(0, w.Sq, size=n_random))
+        rows += [(b, t) for t in sorted(ts)]
+    return rows
+
+
+def run_and_check(name, decode, n_random, b_subset=None):
+    import relative_position_bias_rba_amd as rba
+    w = CONFIGS[name]
+    say(f"[{name}] generating inputs {w}")
+    inp = make_inputs(w)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    say(f"[{name}] relproj + attention on the GPU")
+    R = rba.relproj(d["r"], d["P"])
+    if decode:
+        o, lse = rba.attn_decode(d["q"], d["k"], d["v"], R, window=w.window, log_scale_base=w.log_scale_base,
+                                 num_splits=0, return_lse=True)
+    else:
+        o, lse = rba.attn_prefill(d["q"], d["k"], d["v"], R, window=w.window, log_scale_base=w.log_scale_base,
+                                  return_lse=True)
+    torch.cuda.synchronize()
+    del R
+    o = o.cpu()
+    lse = lse.cpu()
+    del d
+    torch.cuda.empty_cache()
+    rows = rows_for(w, n_random, w.seed)
+    if b_subset is not None:
+        rows = [(b, t) for (b, t) in rows if b in b_subset]
+    say(f"[{name}] oracle on {len(rows)} rows")
+
+    def R_row(b, t):
+        return oracle.relproj(inp["r"][b, t], inp["P"])   # [Hq, E] in fp64
+
+    wo, wl = oracle.attention_rows(inp["q"], inp["k"], inp["v"], R_row, rows, window=w.window,
+                                   log_scale_base=w.log_scale_base)
+    got = np.stack([o[b, t].double().numpy() for b, t in rows])
+    got_l = np.stack([lse[b, :, t].double().numpy() for b, t in rows])
+    dd = np.abs(got - wo)
+    say(f"[{name}] o max|d|={dd.max():.3e} mean|d|={dd.mean():.3e}; "
+        f"lse max|d|={np.abs(got_l - wl).max():.3e}")
+    assert np.all(np.isfinite(got))
+    assert dd.max() <= 2e-2 and dd.mean() <= 2e-3
+    assert np.abs(got_l - wl).max() <= 2e-2
+
+
+def test_c2_swa_prefill_fullsize():
+    run_and_check("c2_swa_prefill", False, 24)
+
+
+def test_c3_full_prefill_fullsize():
+    run_and_check("c3_full_prefill", False, 10)
+
+
+def test_c4_decode_swa_fullsize():
+    run_and_check("c4_decode_swa", True, 0, b_subset={0, 17, 63})
+
+
+def test_c4_decode_full_fullsize():
+    run_and_check("c4_decode_full", True, 0, b_subset={0, 40, 63})
+
+
+def test_c5_long_decode_fullsize():
+    run_and_check("c5_long_decode", True, 0)

@@ -1,0 +1,322 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: fp32 paths max|d| <= 1e-5; bf16 paths max|d| <= 2e-2 and
+mean|d| <= 2e-3; masking and bucket indexing exact (one-hot tests).
+Small cases compare every output element; the full-size workloads run in the
+launch configuration the benchmark times and compare sampled rows.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS, make_inputs
+from workloads.configs import scaled
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def rba():
+    import relative_position_bias_rba_amd as m  # fails loudly if librba.so is missing
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def check(name, got, want, fp32, extra_tol=None):
+    g = got.detach().double().cpu().numpy() if hasattr(got, "detach") else np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    assert g.shape == w.shape, (g.shape, w.shape)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite output"
+    d = np.abs(g - w)
+    mx, mean = float(d.max()), float(d.mean())
+    rel = float(np.linalg.norm(g - w) / max(np.linalg.norm(w), 1e-30))
+    say(f"[{name}] max|d|={mx:.3e} mean|d|={mean:.3e} rel_l2={rel:.3e}")
+    if fp32:
+        assert mx <= (1e-5 if extra_tol is None else extra_tol), name
+    else:
+        assert mx <= 2e-2 and mean <= 2e-3, name
+    return mx, mean
+
+
+def to_dev(inp):
+    return {k: v.to(DEV) for k, v in inp.items()}
+
+
+def small(w, **over):
+    return scaled(w, **over)
+
+
+# --------------------------------------------------------------------------- relproj
+
+@pytest.mark.parametrize("T,Hq,r_dim,E,dt,odt", [
+    (256, 4, 32, 64, torch.float32, torch.float32),
+    (1000, 8, 64, 512, torch.bfloat16, torch.bfloat16),
+    (77, 3, 40, 100, torch.bfloat16, torch.bfloat16),
+    (300, 5, 17, 37, torch.float32, torch.float32),
+    (129, 2, 128, 200, torch.bfloat16, torch.float32),
+    (1, 64, 64, 512, torch.bfloat16, torch.bfloat16),
+])
+def test_relproj_parity(T, Hq, r_dim, E, dt, odt):
+    say(f"relproj T={T} Hq={Hq} r_dim={r_dim} E={E} {dt}->{odt}")
+    g = torch.Generator().manual_seed(T * 7 + E)
+    r = torch.randn(T, r_dim, generator=g).to(dt)
+    P = (torch.randn(Hq, r_dim, E, generator=g) * 0.02).to(dt)
+    R = rba().relproj(r.to(DEV), P.to(DEV), out_dtype=odt)
+    torch.cuda.synchronize()
+    want = oracle.relproj(r, P)
+    fp32 = odt == torch.float32 and dt == torch.float32
+    if odt == torch.bfloat16:
+        # one bf16 rounding of the fp32 sum: |d| <= 2^-8 |R| (+ fp32 sum error)
+        g_ = R.double().cpu().numpy()
+        assert np.all(np.abs(g_ - want) <= np.abs(want) * 2.0 ** -8 + 1e-5)
+    check(f"relproj {T}x{Hq}x{r_dim}x{E}", R, want, fp32)
+
+
+# --------------------------------------------------------------------------- prefill, small shapes, every element
+
+def run_path(inp, w, *, decode=False, splits=0, return_lse=True):
+    m = rba()
+    d = to_dev(inp)
+    R = m.relproj(d["r"], d["P"])
+    fn = m.attn_decode if decode else m.attn_prefill
+    kw = dict(window=w.window, log_scale_base=w.log_scale_base, return_lse=return_lse)
+    if decode:
+        kw["num_splits"] = splits
+    out = fn(d["q"], d["k"], d["v"], R, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_full(inp, w):
+    R = oracle.relproj(inp["r"], inp["P"])
+    return oracle.attention(inp["q"], inp["k"], inp["v"], R, window=w.window, log_scale_base=w.log_scale_base)
+
+
+def test_c1_tiny_fp32_full():
+    w = CONFIGS["c1_tiny_fp32"]
+    say(f"prefill {w}")
+    inp = make_inputs(w)
+    o, lse = run_path(inp, w)
+    wo, wl = oracle_full(inp, w)
+    check("c1 o", o, wo, True)
+    check("c1 lse", lse, wl, True)
+
+
+PREFILL_CASES = [
+    # name, overrides of the windowed bf16 workload
+    ("swa_ragged", dict(B=1, Sq=300, Skv=300, Hq=16, Hkv=2, window=96, E=64)),
+    ("full_logscale", dict(B=2, Sq=517, Skv=517, Hq=16, Hkv=2, window=0, E=64, log_scale_base=4096.0)),
+    ("swa_wide_extent", dict(B=1, Sq=400, Skv=400, Hq=8, Hkv=1, window=70, E=200)),
+    ("ext_not_mult8", dict(B=1, Sq=333, Skv=333, Hq=8, Hkv=2, window=0, E=100)),
+    ("gqa4", dict(B=1, Sq=260, Skv=260, Hq=8, Hkv=2, window=0, E=64)),
+    ("mha", dict(B=1, Sq=200, Skv=200, Hq=2, Hkv=2, window=50, E=32)),
+    ("gqa16", dict(B=1, Sq=150, Skv=150, Hq=32, Hkv=2, window=0, E=64)),
+    ("sq_lt_skv", dict(B=2, Sq=77, Skv=333, Hq=16, Hkv=2, window=128, E=64, log_scale_base=64.0)),
+    ("window1", dict(B=1, Sq=130, Skv=130, Hq=8, Hkv=1, window=1, E=16)),
+    ("tiny", dict(B=1, Sq=1, Skv=1, Hq=8, Hkv=1, window=0, E=8)),
+]
+
+
+@pytest.mark.parametrize("name,over", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_bf16_small(name, over):
+    w = small(CONFIGS["c2_swa_prefill"], **over)
+    say(f"prefill {name}: {w}")
+    inp = make_inputs(w)
+    o, lse = run_path(inp, w)
+    wo, wl = oracle_full(inp, w)
+    check(f"{name} o", o, wo, False)
+    check(f"{name} lse", lse, wl, True, extra_tol=2e-2)
+
+
+def test_prefill_fp32_variants():
+    base = CONFIGS["c1_tiny_fp32"]
+    for over in (dict(Sq=200, Skv=200, window=33, E=50), dict(B=2, Sq=70, Skv=150, Hq=8, Hkv=2, log_scale_base=16.0),
+                 dict(Sq=100, Skv=100, Hq=6, Hkv=3, E=7, window=0)):
+        w = small(base, **over)
+        say(f"prefill fp32 {w}")
+        inp = make_inputs(w)
+        o, lse = run_path(inp, w)
+        wo, wl = oracle_full(inp, w)
+        check("fp32 o", o, wo, True)
+        check("fp32 lse", lse, wl, True)
+
+
+def test_prefill_without_bias_and_noncontiguous_q():
+    m = rba()
+    w = small(CONFIGS["c2_swa_prefill"], B=1, Sq=200, Skv=200, Hq=16, Hkv=2, window=0, E=64)
+    inp = make_inputs(w)
+    d = to_dev(inp)
+    # q as a strided view into a wider buffer
+    qbig = torch.zeros(1, 200, 16, 256, dtype=torch.bfloat16, device=DEV)
+    qbig[..., 64:192] = d["q"]
+    qv = qbig[..., 64:192]
+    o = m.attn_prefill(qv, d["k"], d["v"], None, window=0)
+    torch.cuda.synchronize()
+    wo, _ = oracle.attention(inp["q"], inp["k"], inp["v"], None)
+    check("nobias strided", o, wo, False)
+
+
+# --------------------------------------------------------------------------- decode, small shapes
+
+DECODE_CASES = [
+    ("full", dict(B=3, Sq=9, Skv=700, window=0, log_scale_base=0.0)),
+    ("swa", dict(B=3, Sq=9, Skv=1000, window=256, log_scale_base=0.0)),
+    ("full_log", dict(B=2, Sq=1, Skv=1500, window=0, log_scale_base=4096.0)),
+    ("swa_log", dict(B=2, Sq=5, Skv=777, window=300, log_scale_base=64.0)),
+]
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 0])
+@pytest.mark.parametrize("name,over", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_small(name, over, splits):
+    w = small(CONFIGS["c4_decode_full"], Hq=16, Hkv=2, E=64, **over)
+    say(f"decode {name} splits={splits}: {w}")
+    inp = make_inputs(w)
+    o, lse = run_path(inp, w, decode=True, splits=splits)
+    wo, wl = oracle_full(inp, w)
+    check(f"decode {name}/{splits} o", o, wo, False)
+    check(f"decode {name}/{splits} lse", lse, wl, True, extra_tol=2e-2)
+
+
+def test_decode_split_invariance_and_prefill_agreement():
+    m = rba()
+    w = small(CONFIGS["c4_decode_full"], B=2, Sq=9, Skv=1200, Hq=16, Hkv=2, E=64, window=0)
+    inp = make_inputs(w)
+    outs = [run_path(inp, w, decode=True, splits=s) for s in (1, 2, 3, 7, 19)]
+    o1, l1 = outs[0]
+    for o, l in outs[1:]:
+        assert torch.max(torch.abs(l - l1)).item() <= 1e-5
+        assert torch.max(torch.abs(o.float() - o1.float())).item() <= 2.0 ** -7 * max(1.0, o1.float().abs().max().item())
+    # decode with Sq rows equals prefill of the same rows
+    op, lp = run_path(inp, w, decode=False)
+    assert torch.max(torch.abs(lp - l1)).item() <= 1e-5
+
+
+# --------------------------------------------------------------------------- combine kernel on its own
+
+def test_combine_kernel_parity():
+    m = rba()
+    g = torch.Generator().manual_seed(5)
+    S, B, Sq, Hq = 6, 2, 3, 8
+    op = torch.randn(S, B, Sq, Hq, 128, generator=g)
+    lp = torch.randn(S, B, Sq, Hq, generator=g) * 3
+    lp[1, 0] = -math.inf            # an empty split for some rows
+    lp[:, 1, 2, 5] = -math.inf      # a row with no visible key at all
+    q_like = torch.empty(B, Sq, Hq, 128, dtype=torch.float32, device=DEV)
+    k_like = torch.empty(B, Sq, 1, 128, dtype=torch.float32, device=DEV)
+    o, lse = m.splitkv_combine(op.to(DEV), lp.to(DEV), q_like, k_like, return_lse=True)
+    torch.cuda.synchronize()
+    wo, wl = oracle.lse_combine(op.numpy(), lp.numpy())
+    check("combine o", o, wo, True)
+    got_l = lse.cpu().numpy().transpose(0, 2, 1)
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(wl))
+    fin = np.isfinite(wl)
+    assert np.max(np.abs(got_l[fin] - wl[fin])) <= 1e-5
+
+
+# --------------------------------------------------------------------------- exact structure tests
+
+@pytest.mark.parametrize("dstar,window", [(0, 0), (1, 0), (63, 0), (17, 40), (5, 3)])
+@pytest.mark.parametrize("decode", [False, True])
+def test_one_hot_bias_exact(dstar, window, decode):
+    """q = k = 0, R one-hot 30 at distance d*, v coded by position in two
+    bf16-exact channels: o must decode exactly to key p - d* (or equal the
+    plain mean when that key is not visible)."""
+    m = rba()
+    S, E, Hq, Hkv = 600, 64, 16, 2
+    Sq = 9 if decode else S
+    q = torch.zeros(2, Sq, Hq, 128, dtype=torch.bfloat16)
+    k = torch.zeros(2, S, Hkv, 128, dtype=torch.bfloat16)
+    v = torch.zeros(2, S, Hkv, 128, dtype=torch.bfloat16)
+    j = torch.arange(S)
+    v[:, :, :, 0] = (j % 256).to(torch.bfloat16)[None, :, None]
+    v[:, :, :, 1] = (j // 256).to(torch.bfloat16)[None, :, None]
+    v[:, :, 1, 2] = 1.0
+    R = torch.zeros(2, Sq, Hq, E, dtype=torch.bfloat16)
+    R[..., dstar] = 30.0
+    d = {n: t.to(DEV) for n, t in dict(q=q, k=k, v=v, R=R).items()}
+    if decode:
+        o = m.attn_decode(d["q"], d["k"], d["v"], d["R"], window=window, num_splits=3)
+    else:
+        o = m.attn_prefill(d["q"], d["k"], d["v"], d["R"], window=window)
+    torch.cuda.synchronize()
+    o = o.float().cpu()
+    wo, _ = oracle.attention(q, k, v, R, window=window)
+    exact_rows = 0
+    for t in range(Sq):
+        p = S - Sq + t
+        lo = 0 if window == 0 else max(0, p - window + 1)
+        if p - dstar >= lo:
+            target = p - dstar
+            assert torch.all(o[:, t, :, 0] == float(target % 256)), (t, o[:, t, :, 0])
+            assert torch.all(o[:, t, :, 1] == float(target // 256))
+            exact_rows += 1
+    assert exact_rows > 0
+    check(f"onehot d*={dstar} W={window}", o, wo, False)
+
+
+def test_window_one_returns_v_exactly():
+    m = rba()
+    w = small(CONFIGS["c2_swa_prefill"], B=1, Sq=333, Skv=333, Hq=16, Hkv=2, window=1, E=64)
+    inp = make_inputs(w)
+    o = run_path(inp, w, return_lse=False)
+    G = 8
+    vv = inp["v"].repeat_interleave(G, dim=2)
+    assert torch.equal(o.cpu(), vv)
+
+
+def test_future_keys_never_leak():
+    """Make every future key dominant (k_j = 4 q for j > p): any leak through
+    the causal mask would change o far beyond tolerance."""
+    w = small(CONFIGS["c2_swa_prefill"], B=1, Sq=256, Skv=256, Hq=8, Hkv=8, window=0, E=32)
+    inp = make_inputs(w)
+    # one query vector per head shared by all rows; keys equal 4 q
+    q = inp["q"].clone()
+    q[:] = q[:, :1]
+    inp["q"] = q
+    inp["k"] = (4 * q.float()).to(torch.bfloat16)
+    o, _ = run_path(inp, w)
+    wo, _ = oracle_full(inp, w)
+    check("no-leak", o, wo, False)
+
+
+def test_uniform_weights_visible_mean():
+    """q = k = 0, R = 0: o is the mean of the visible v (exact counting)."""
+    m = rba()
+    S, Hq, Hkv = 500, 8, 1
+    for window in (0, 37, 64, 65):
+        q = torch.zeros(1, S, Hq, 128, dtype=torch.bfloat16, device=DEV)
+        k = torch.zeros(1, S, Hkv, 128, dtype=torch.bfloat16, device=DEV)
+        v = torch.randn(1, S, Hkv, 128, generator=torch.Generator().manual_seed(window)).to(torch.bfloat16)
+        o, lse = m.attn_prefill(q, k, v.to(DEV), None, window=window, return_lse=True)
+        torch.cuda.synchronize()
+        vd = v.double()[0, :, 0]
+        cs = torch.cat([torch.zeros(1, 128, dtype=torch.float64), torch.cumsum(vd, 0)])
+        pos = torch.arange(S)
+        lo = torch.zeros(S, dtype=torch.long) if window == 0 else torch.clamp(pos - window + 1, min=0)
+        n = (pos - lo + 1).double()
+        mean = (cs[pos + 1] - cs[lo]) / n[:, None]
+        check(f"mean W={window}", o[0, :, 0], mean.numpy(), False)
+        assert torch.max(torch.abs(lse[0, 0].cpu().double() - torch.log(n))).item() <= 1e-5
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = small(CONFIGS["c2_swa_prefill"], B=1, Sq=700, Skv=700, Hq=16, Hkv=2, window=200, E=64)
+    inp = make_inputs(w)
+    a, la = run_path(inp, w)
+    b, lb = run_path(inp, w)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    wd = small(CONFIGS["c4_decode_full"], B=2, Sq=9, Skv=3000, Hq=16, Hkv=2, E=64)
+    inpd = make_inputs(wd)
+    a, la = run_path(inpd, wd, decode=True, splits=5)
+    b, lb = run_path(inpd, wd, decode=True, splits=5)
+    assert torch.equal(a, b) and torch.equal(la, lb)
