@@ -72,7 +72,7 @@ typedef struct rba_attn_args {
     rba_dtype dt;
     int B, Sq, Skv, Hq, Hkv, d, E;
     int window;            /* 0 = full causal; > 0: key visible iff 0 <= p - j < window */
-    float scale;           /* multiplies q.k only, usually 1/sqrt(d) */
+    float scale;           /* multiplies q.k only; finite and > 0, usually 1/sqrt(d) */
     float log_scale_base;  /* 0 = off; > 1: logits multiplied by ln(p+1)/ln(base) */
     const void *q, *k, *v;
     const void *R;

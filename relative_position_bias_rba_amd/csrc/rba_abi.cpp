@@ -35,7 +35,7 @@ rba_status validate_attn(const rba_attn_args *a) {
     if (a->Hq % a->Hkv != 0) return RBA_E_INVALID;
     if (a->Sq > a->Skv) return RBA_E_INVALID;
     if (a->window < 0) return RBA_E_INVALID;
-    if (!isfinite(a->scale)) return RBA_E_INVALID;
+    if (!isfinite(a->scale) || !(a->scale > 0.f)) return RBA_E_INVALID;
     if (!(a->log_scale_base == 0.f || (isfinite(a->log_scale_base) && a->log_scale_base > 1.f)))
         return RBA_E_INVALID;
     if (a->R != nullptr && a->E < 1) return RBA_E_INVALID;

@@ -70,6 +70,8 @@ def test_validation_rejects_bad_shapes():
     a = make_args(q, k, v, R, o); a.E = 0; cases.append((a, RBA_E_INVALID))
     a = make_args(q, k, v, R, o); a.log_scale_base = 0.5; cases.append((a, RBA_E_INVALID))
     a = make_args(q, k, v, R, o); a.scale = float("nan"); cases.append((a, RBA_E_INVALID))
+    a = make_args(q, k, v, R, o); a.scale = 0.0; cases.append((a, RBA_E_INVALID))
+    a = make_args(q, k, v, R, o); a.scale = -0.1; cases.append((a, RBA_E_INVALID))
     a = make_args(q, k, v, R, o); a.dt = 7; cases.append((a, RBA_E_UNSUPPORTED))
     a = make_args(q, k, v, R, o); a.Hq = 512; a.Hkv = 1; cases.append((a, RBA_E_UNSUPPORTED))
     a = make_args(q, k, v, R, o); a.B = -1; cases.append((a, RBA_E_INVALID))
