@@ -140,7 +140,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int hh = lane >> 5;     // lane half
     const int lc = lane & 31;     // lane column
 
@@ -511,26 +511,34 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         kband = min(max(first, kb), ke);
     }
     const int n_band = ke - kband;
-    auto tile_of = [&](int i) {
-        const int c0 = (int)((int64_t)i * n_band / n_it);
-        const int c1 = (int)((int64_t)(i + 1) * n_band / n_it);
-        return c1 > c0 ? kband + c0 : kb + (i - c0);
+    // iteration i is banded iff floor((i+1) nb / n) > floor(i nb / n); scalar,
+    // incremental
+    int g_rem = 0, g_cnt = 0, g_idx = 0;
+    auto next_tile = [&]() {
+        const bool bnd = g_rem + n_band >= n_it;
+        const int kt = bnd ? kband + g_cnt : kb + g_idx - g_cnt;
+        g_rem += n_band;
+        if (g_rem >= n_it) {
+            g_rem -= n_it;
+            ++g_cnt;
+        }
+        ++g_idx;
+        return kt;
     };
 
+    int kt = n_it > 0 ? next_tile() : 0;
     if (n_it > 0) {
-        const int kt0 = tile_of(0);
-        stage_k(kt0, 0);
-        load_v(kt0);
-        if (banded(kt0)) stage_slab(kt0, 0);
+        stage_k(kt, 0);
+        load_v(kt);
+        if (banded(kt)) stage_slab(kt, 0);
         store_v();
         wait_vmem();
     }
     __syncthreads();
-    int kt = n_it > 0 ? tile_of(0) : 0;
     for (int it = 0; it < n_it; ++it) {
         const int cur = it & 1;
         const bool nxt = it + 1 < n_it;
-        const int kn = nxt ? tile_of(it + 1) : kt;
+        const int kn = nxt ? next_tile() : kt;
         if (nxt) {
             stage_k(kn, cur ^ 1);
             load_v(kn);
@@ -634,7 +642,7 @@ hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stre
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
     switch (v) {
-        case AttnVariant::BF16_WIDE:    // 8 waves: 256 columns, double-buffered bias slab
+        case AttnVariant::BF16_WIDE:    // 8 waves, 256 columns, two bias slab buffers
             hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 8, true>), grid, dim3(512), 0, stream, p);
             break;
         case AttnVariant::BF16_NARROW:  // 4 waves: 128 columns, small LDS footprint
