@@ -92,6 +92,14 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier after this wave's LDS accesses have completed.  The
+// compiler-level memory fences keep LDS accesses from moving across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit data format
 
@@ -108,6 +116,25 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
 __device__ __forceinline__ void dma16(rsrc_t r, unsigned voff, void *lds_wave) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_wave, 16, voff, 0, 0,
                                              0);
+}
+
+// Buffer descriptor words for dma16_untracked (same layout as make_rsrc).
+__device__ __forceinline__ u32x4 make_rsrc_words(const void *base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, (unsigned)n, (unsigned)kRsrcFlags};
+}
+
+// dma16 written as inline assembly.  The compiler does not see this load, so
+// it never makes later LDS reads wait for it (it cannot tell which LDS bytes
+// a direct-to-LDS load writes and would otherwise wait for all of them);
+// the caller waits (vmcnt(0)) before the barrier that hands the data over.
+__device__ __forceinline__ void dma16_untracked(u32x4 rsrc, unsigned voff, const void *lds_wave) {
+    const unsigned m0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void *)lds_wave;
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(m0)
+                 : "memory", "m0");
 }
 
 template <typename T, int NW, bool SLAB2>
@@ -600,6 +627,466 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     }
 }
 
+// Prefill with 8 waves in two groups (waves 0-3 and 4-7; each SIMD holds one
+// wave of each).  Time is cut into phases separated by workgroup barriers.
+// In every phase one group runs its matrix work (PV of its previous tile and
+// S^T = K Q^T of the current one) while the other group runs the softmax of
+// its latest scores, so the matrix cores and the vector ALUs of each SIMD
+// work at the same time.  Roles swap every phase:
+//   group 0: phase 2t   MFMA [PV(t-1), QK(t)]   phase 2t+1 VALU [softmax(t)]
+//   group 1: phase 2t   VALU [softmax(t-1)]     phase 2t+1 MFMA [PV(t-1), QK(t)]
+// Each group runs its own copy of the phase loop with its roles fixed at
+// compile time.  All staging is global -> LDS DMA issued by group 0 between
+// the matrix instructions of its even phases and awaited at the end of the
+// following odd phase: K(t+1), V(t) and the bias windows of both groups
+// (group 0's for tile t+1, group 1's for tile t).  V is kept row-major in LDS
+// (16-byte chunks XOR-swizzled by row) and read as the PV A-operand with the
+// LDS transpose read, so it never passes through registers.  LDS regions are
+// padded to whole DMA instructions so no lane needs masking.
+__global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParams p) {
+    typedef __bf16 T;
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    constexpr int ES = 2;
+    constexpr int N = 64;                        // keys per tile
+    constexpr int KT = N / 32;
+    constexpr int CH = 8;                        // bf16 per 16-byte chunk
+    constexpr int SW = N + CH;                   // slab row: the N entries a row needs, chunk-aligned
+    constexpr int NCH = SW / CH;
+    constexpr int HROWS = 128;                   // slab rows (query columns) of one group
+    constexpr int HCH = HROWS * NCH;             // slab chunks of one group
+    constexpr int CPR = D * ES / 16;             // 16-byte chunks per K/V row
+    constexpr int CPRP = CPR + 1;                // K rows carry one padding chunk
+    constexpr int KS = CPRP * CH;
+    constexpr int KCH = N * CPRP;
+    constexpr int VCH = N * CPR;
+    constexpr int GT = 256;                      // threads of the issuing group
+    constexpr int NKI = (KCH + GT - 1) / GT;     // 5
+    constexpr int NVI = VCH / GT;                // 4
+    constexpr int NSI = (HCH + GT - 1) / GT;     // 5 per group half
+    constexpr int NSLOT = NKI + NVI + 2 * NSI;   // DMA instructions per issuing lane and phase
+    static_assert(NKI == 5 && NVI * GT == VCH && NSI == 5, "staging split");
+
+    __shared__ __attribute__((aligned(16))) T sK[2][NKI * GT * CH];
+    __shared__ __attribute__((aligned(16))) T sV[2][N * D];
+    __shared__ __attribute__((aligned(16))) T sR[2][2][NSI * GT * CH];   // [group][buffer]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+    const int grp = wave >> 2;
+    const int gw = wave & 3;
+    const int hh = lane >> 5;
+    const int lc = lane & 31;
+
+    // ------------------------------------------------------------ work item
+    const int per_bh = p.nqb * p.splits;
+    const int total = p.B * p.Hkv * per_bh;
+    int item = blockIdx.x;
+    if ((total & 7) == 0) item = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    const int bh = item / per_bh;
+    const int rem = item - bh * per_bh;
+    const int qb = p.nqb - 1 - rem / p.splits;
+    const int sp = rem % p.splits;
+    const int b = bh / p.Hkv;
+    const int hkv = bh - b * p.Hkv;
+    const int t0 = qb * p.QB;
+    const int nrows = min(p.QB, p.Sq - t0);
+    const int pos0 = p.Skv - p.Sq;
+    const int p_min = pos0 + t0;
+    const int p_max = p_min + nrows - 1;
+    const int W = p.window;
+    const int lo_key = W > 0 ? max(0, p_min - W + 1) : 0;
+    const int kt_lo = lo_key / N;
+    const int n_t = p_max / N - kt_lo + 1;
+    const int kb = kt_lo + (int)((int64_t)sp * n_t / p.splits);
+    const int ke = kt_lo + (int)((int64_t)(sp + 1) * n_t / p.splits);
+    const int ncols = p.G * p.QB;
+    const bool has_bias = p.R != nullptr && p.E > 0;
+
+    const T *__restrict__ gk = (const T *)p.k + (int64_t)b * p.ks0 + (int64_t)hkv * p.ks2;
+    const T *__restrict__ gv = (const T *)p.v + (int64_t)b * p.vs0 + (int64_t)hkv * p.vs2;
+
+    // ------------------------------------------------------------ this lane's query column
+    const int col = wave * 32 + lc;
+    const int hl = col / p.QB;
+    const int qi = col - hl * p.QB;
+    const bool cvalid = col < ncols && qi < nrows;
+    const int tq = t0 + qi;
+    const int hq = hkv * p.G + min(hl, p.G - 1);
+    const int prow = p_min + qi;
+    // log-scale factor, kept > 0 so that masked -inf logits stay -inf
+    const float fls = p.inv_ln_base > 0.f ? fmaxf(logf((float)prow + 1.f) * p.inv_ln_base, 1e-30f) : 1.f;
+    const float amul = p.scale_log2e * fls;
+    const float bmul = kLog2e * fls;
+    const bool wave_active = wave * 32 < ncols;
+    const int rb = (prow - N + 1) & ~(CH - 1);
+
+    bf16x8 qf[8];
+    {
+        const T *qp = (const T *)p.q + (int64_t)b * p.qs0 + (int64_t)tq * p.qs1 + (int64_t)hq * p.qs2;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) qf[k] = cvalid ? *(const bf16x8 *)(qp + 16 * k + 8 * hh) : bf16x8{};
+        // Settle the loads here: otherwise the compiler's wait for them sits
+        // inside the phase loop, where it would also wait for the DMA.
+#pragma unroll
+        for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(qf[k]));
+    }
+
+    f32x16 O[4];
+    f32x16 S[KT];
+    bf16x8 P[2 * KT];
+    float m = -INFINITY, l = 0.f;
+    float o_scale = 1.f;        // rescale of O owed by the last softmax
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) O[dt] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < 2 * KT; ++i) P[i] = bf16x8{};
+
+    // ------------------------------------------------------------ staging offsets (group 0 lanes)
+    // K: LDS chunk L holds chunk L % CPRP of key row lds_key_row(L / CPRP);
+    // the padding chunk reloads chunk 0.  Chunks past the tile land in the
+    // padding of the buffer.
+    const int gl = gw * 64 + lane;               // lane index within the issuing group
+    unsigned kvo[NKI];
+#pragma unroll
+    for (int i = 0; i < NKI; ++i) {
+        const int L = i * GT + gl;
+        const int R = L / CPRP, pc = L - R * CPRP;
+        kvo[i] = (unsigned)((lds_key_row(R & 63) * (int)p.ks1 + (pc < CPR ? pc : 0) * CH) * ES);
+    }
+    // V: LDS chunk L holds chunk (L % 16) ^ 4 (r % 4) of key row r = L / 16.
+    unsigned vvo[NVI];
+#pragma unroll
+    for (int i = 0; i < NVI; ++i) {
+        const int L = i * GT + gl;
+        const int r = L >> 4, c = (L & 15) ^ ((r & 3) << 2);
+        vvo[i] = (unsigned)((r * (int)p.vs1 + c * CH) * ES);
+    }
+    // Slab of group g: chunk L holds chunk L % NCH of the bias window of
+    // query column g * HROWS + L / NCH; -j0 is added per tile.
+    unsigned svo[2][NSI];
+    const int64_t rbase = (int64_t)b * p.Rs0 + (int64_t)t0 * p.Rs1 + (int64_t)hkv * p.G * p.Rs2;
+    const int64_t rspan = ((int64_t)(nrows - 1) * p.Rs1 + (int64_t)(p.G - 1) * p.Rs2 + p.E) * ES;
+    const rsrc_t rR = make_rsrc(has_bias ? (const T *)p.R + rbase : (const T *)p.q, has_bias ? rspan : 0);
+    const u32x4 rR4 = make_rsrc_words(has_bias ? (const T *)p.R + rbase : (const T *)p.q, has_bias ? rspan : 0);
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int i = 0; i < NSI; ++i) {
+            const int L = i * GT + gl;
+            const int row = g * HROWS + L / NCH, ch = L % NCH;
+            const int rhl = row / p.QB, rqi = row - rhl * p.QB;
+            const bool live = L < HCH && row < ncols && rqi < nrows;
+            const int rrb = (p_min + rqi - N + 1) & ~(CH - 1);
+            // dead chunks point far past the span: they read zeros
+            svo[g][i] = live ? (unsigned)(((int64_t)rqi * p.Rs1 + (int64_t)rhl * p.Rs2 + rrb + ch * CH) * ES)
+                             : 0x80000000u;
+        }
+
+    // ------------------------------------------------------------ tile sequence (banded tiles spread out)
+    const int n_it = ke - kb;
+    int kband = ke;
+    if (has_bias) {
+        const int x = p_min - N + 1 - p.E;
+        const int first = x < 0 ? 0 : x / N + 1;
+        kband = min(max(first, kb), ke);
+    }
+    const int n_band = ke - kband;
+    // iteration i is banded iff floor((i+1) nb / n) > floor(i nb / n); scalar, incremental
+    int g_rem = 0, g_cnt = 0, g_idx = 0;
+    auto next_tile = [&]() __attribute__((always_inline)) {
+        const bool bnd = g_rem + n_band >= n_it;
+        const int kt = bnd ? kband + g_cnt : kb + g_idx - g_cnt;
+        g_rem += n_band;
+        if (g_rem >= n_it) {
+            g_rem -= n_it;
+            ++g_cnt;
+        }
+        ++g_idx;
+        return kt;
+    };
+    auto banded = [&](int kt) __attribute__((always_inline)) { return has_bias && (p_min - (kt * N + N - 1) < p.E); };
+    // K/V descriptors of a key tile: rows from j0 to the end of the sequence
+    // (the host guarantees these spans fit 31 bits).
+    const unsigned kstep = (unsigned)(N * (int)p.ks1 * ES), vstep = (unsigned)(N * (int)p.vs1 * ES);
+    const unsigned kspan = (unsigned)(((p.Skv - 1) * (int)p.ks1 + D) * ES);
+    const unsigned vspan = (unsigned)(((p.Skv - 1) * (int)p.vs1 + D) * ES);
+    const u32x4 rk0 = make_rsrc_words(gk, kspan), rv0 = make_rsrc_words(gv, vspan);
+    auto tile_rsrc = [&](u32x4 r0, unsigned step, unsigned span, int kt) __attribute__((always_inline)) {
+        const unsigned off = (unsigned)kt * step;
+        const uint64_t a = ((uint64_t)r0[1] << 32 | r0[0]) + off;
+        return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, span - off, r0[3]};
+    };
+
+    // DMA plan of the current even phase (wave-uniform)
+    bool dk = false, dv = false, ds0 = false, ds1 = false;
+    int kbuf = 0, vbuf = 0, s0buf = 0, s1buf = 0;
+    unsigned s0off = 0, s1off = 0;
+    u32x4 rk = rk0, rv = rv0;
+    auto issue = [&](int s) __attribute__((always_inline)) {
+        if (s < NKI) {
+            if (dk) dma16_untracked(rk, kvo[s], &sK[kbuf][(s * GT + gw * 64) * CH]);
+        } else if (s < NKI + NVI) {
+            const int i = s - NKI;
+            if (dv) dma16_untracked(rv, vvo[i], &sV[vbuf][(i * GT + gw * 64) * CH]);
+        } else if (s < NKI + NVI + NSI) {
+            const int i = s - NKI - NVI;
+            if (ds0) dma16_untracked(rR4, svo[0][i] + s0off, &sR[0][s0buf][(i * GT + gw * 64) * CH]);
+        } else {
+            const int i = s - NKI - NVI - NSI;
+            if (ds1) dma16_untracked(rR4, svo[1][i] + s1off, &sR[1][s1buf][(i * GT + gw * 64) * CH]);
+        }
+    };
+    // bias rows not 16-byte aligned: element loads through registers
+    auto slab_fallback = [&](int g, int buf, int kt) __attribute__((always_inline)) {
+        const unsigned eoff = (unsigned)(-kt * N * ES);
+#pragma unroll
+        for (int i = 0; i < NSI; ++i) {
+            u32x4 val = u32x4{};
+#pragma unroll
+            for (int x = 0; x < CH; ++x)
+                val[x >> 1] |= (unsigned)__builtin_amdgcn_raw_buffer_load_b16(rR, svo[g][i] + eoff + x * ES, 0, 0)
+                               << (16 * (x & 1));
+            *(u32x4 *)&sR[g][buf][(i * GT + gl) * CH] = val;
+        }
+    };
+    // Sets up (and for unaligned bias rows, performs) the staging of even
+    // phase 2t: K(t+1), V(t), group 0's bias windows of tile t+1 and group
+    // 1's of tile t.  w1, w2 are the key tiles of sequence indices t, t+1.
+    auto plan_even = [&](int t, int w1, int w2) __attribute__((always_inline)) {
+        dk = t + 1 < n_it;
+        kbuf = (t + 1) & 1;
+        rk = tile_rsrc(rk0, kstep, kspan, w2);
+        dv = t >= 1 && t < n_it;
+        vbuf = t & 1;
+        rv = tile_rsrc(rv0, vstep, vspan, w1);
+        ds0 = t + 1 < n_it && banded(w2);
+        s0buf = (t + 1) & 1;
+        s0off = (unsigned)(-w2 * N * ES);
+        ds1 = t < n_it && banded(w1);
+        s1buf = t & 1;
+        s1off = (unsigned)(-w1 * N * ES);
+        if (!p.r_vec) {
+            if (ds0) slab_fallback(0, s0buf, w2);
+            if (ds1) slab_fallback(1, s1buf, w1);
+            ds0 = ds1 = false;
+        }
+    };
+
+    // ------------------------------------------------------------ phase work
+    const int kr0 = lds_key_row(mfma_row_key(lc));
+    const int s_lane = (col - grp * HROWS) * SW + (prow - rb) - 16 * hh;
+    // V^T fragment of PV step (u, h2, dt): two transpose reads of 4 keys each.
+    // Lane (g = lane / 16, a = lane % 4, i = lane / 4 % 4) addresses key row
+    // 32u + 16(g / 2) + 8h2 + 4x + i and head-dim entries 32dt + 16(g % 2) + 4a,
+    // and receives key rows of one head-dim entry back.
+    const int tr_i = (lane >> 2) & 3;
+    int vt_off[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+        vt_off[dt] = (16 * hh + tr_i) * D + CH * ((((dt ^ tr_i) << 2) | (((lane >> 4) & 1) << 1) | ((lane >> 1) & 1))) +
+                     4 * (lane & 1);
+
+    // Matrix phase: the 16 PV steps of tile tp, then the 16 QK^T steps of
+    // tile tqk, one MFMA per step, A-operand fragments read LA steps ahead;
+    // with DMA, one staging instruction is issued per step.
+    auto mfma_phase = [&](int tp, int tqk, auto dma_c) __attribute__((always_inline)) {
+        constexpr bool DMA = decltype(dma_c)::value;
+        constexpr int LA = 6;
+        const T *vb = &sV[tp & 1][0];
+        const T *kb_ = &sK[tqk & 1][kr0 * KS];
+        auto trv = [&](const T *ptr) __attribute__((always_inline)) {
+            return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t *)ptr);
+        };
+        auto frag = [&](int st) __attribute__((always_inline)) {
+            if (st < 16) {   // PV step: sub-tile u = st / 8, half h2 = (st / 4) & 1, dims dt = st & 3
+                const T *base = vb + vt_off[st & 3] + (32 * (st >> 3) + 8 * ((st >> 2) & 1)) * D;
+                const bf16x4_t lo = trv(base), hi = trv(base + 4 * D);
+                return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            const int q = st - 16;   // QK step: k-step q / 2, sub-tile q & 1
+            return *(const bf16x8 *)(kb_ + (q & 1) * 32 * KS + 16 * (q >> 1) + 8 * hh);
+        };
+        bf16x8 fr[32];
+#pragma unroll
+        for (int st = 0; st < LA; ++st) fr[st] = frag(st);
+        if (__builtin_amdgcn_ballot_w64(o_scale != 1.f) != 0) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) O[dt] *= o_scale;
+        }
+#pragma unroll
+        for (int st = 0; st < 32; ++st) {
+            if (st + LA < 32) fr[st + LA] = frag(st + LA);
+            if constexpr (DMA) {
+                if (st < NSLOT) issue(st);
+            }
+            if (st < 16) {
+                O[st & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[st], P[st >> 2], O[st & 3], 0, 0, 0);
+            } else {
+                const int q = st - 16;
+                if (q < KT) S[q] = f32x16{};
+                S[q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[st], qf[q >> 1], S[q & 1], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Vector phase: bias, mask, running max and exponentials of tile t
+    // (sequence index), key tile kt.
+    auto softmax = [&](int t, int kt) __attribute__((always_inline)) {
+        const int j0 = kt * N;
+        const bool band = banded(kt);
+        const bool edge = !((j0 + N - 1 <= p_min) && (W == 0 || p_max - j0 < W));
+        float mt = -INFINITY;
+        if (band || edge) {
+            const T *sr = &sR[grp][t & 1][s_lane];
+            const bool partial = p_max - j0 >= p.E;
+            const int elim = prow - j0 - 16 * hh - p.E;   // key offset r of a half has e < E iff r > elim
+            const int dbase = prow - j0 - 16 * hh;        // distance of key offset 0 of this half
+#pragma unroll
+            for (int u = 0; u < KT; ++u) {
+                if (band) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float bias = __builtin_bit_cast(float, (unsigned)__builtin_bit_cast(unsigned short, sr[-(32 * u + r)]) << 16);
+                        if (partial) bias = (32 * u + r > elim) ? bias : 0.f;
+                        S[u][r] = fmaf(bias, bmul, S[u][r] * amul);
+                    }
+                }
+                if (edge) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int dist = dbase - 32 * u - r;
+                        const bool vis = dist >= 0 && (W == 0 || dist < W);
+                        S[u][r] = vis ? S[u][r] : -INFINITY;
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < KT; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, S[u][r]);
+        if (!band) mt *= amul;
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        // The reference max only moves when the tile max exceeds it by more
+        // than kRescaleSlack (alpha = 1 otherwise).
+        const bool grow = mt > m + kRescaleSlack;
+        const float mn = grow ? mt : m;
+        const float alpha = m == -INFINITY ? 0.f : (grow ? fast_exp2(m - mn) : 1.f);
+        m = mn;
+        l *= alpha;
+        o_scale = alpha;        // applied to O at the start of the next matrix phase
+        const float mu = m == -INFINITY ? 0.f : m;
+        const float sa = band ? 1.f : amul;
+        float sum = 0.f;
+#pragma unroll
+        for (int u = 0; u < KT; ++u)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                bf16x8 pb;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) pb[x] = (__bf16)fast_exp2(fmaf(S[u][8 * h2 + x], sa, -mu));
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    sum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[2 * x], pb[2 * x + 1]},
+                                                          bf16x2{(__bf16)1.f, (__bf16)1.f}, sum, false);
+                P[2 * u + h2] = pb;
+            }
+        l += sum;
+    };
+
+    // ------------------------------------------------------------ prologue: first tile
+    int w0 = 0, w1 = 0, w2 = 0;     // key tiles of sequence indices t-1, t, t+1
+    if (n_it > 0) {
+        w1 = next_tile();
+        w2 = n_it > 1 ? next_tile() : 0;
+        if (grp == 0) {
+            // K(0), V(0) and group 0's bias windows of tile 0
+            dk = dv = true;
+            rk = tile_rsrc(rk0, kstep, kspan, w1);
+            rv = tile_rsrc(rv0, vstep, vspan, w1);
+            ds0 = banded(w1);
+            s0off = (unsigned)(-w1 * N * ES);
+            if (ds0 && !p.r_vec) {
+                slab_fallback(0, 0, w1);
+                ds0 = false;
+            }
+#pragma unroll
+            for (int s = 0; s < NKI + NVI + NSI; ++s) issue(s);
+            wait_vmem();
+        }
+    }
+    lds_barrier();
+
+    // ------------------------------------------------------------ phases 2t, 2t+1 for t = 0..n_it
+    auto run = [&](auto grp_c) __attribute__((always_inline)) {
+        constexpr int G = decltype(grp_c)::value;
+        for (int t = 0; t <= n_it && n_it > 0; ++t) {
+            if (t > 0) {          // slide the window to t-1, t, t+1
+                w0 = w1;
+                w1 = w2;
+                w2 = t + 1 < n_it ? next_tile() : 0;
+            }
+            // even phase
+            if constexpr (G == 0) {
+                plan_even(t, w1, w2);
+                // P is zero before the first softmax (PV then adds nothing;
+                // V buffer 0 holds the first tile); the QK after the last
+                // tile is never used.
+                mfma_phase(t >= 1 ? t - 1 : 0, t, std::true_type{});
+            } else {
+                if (wave_active && t >= 1) softmax(t - 1, w0);
+            }
+            lds_barrier();
+            // odd phase
+            if constexpr (G == 0) {
+                if (t < n_it) softmax(t, w1);
+                wait_vmem();      // staging of the even phase has landed
+            } else {
+                if (wave_active) mfma_phase(t >= 1 ? t - 1 : 0, t, std::false_type{});
+            }
+            lds_barrier();
+        }
+    };
+    if (grp == 0)
+        run(std::integral_constant<int, 0>{});
+    else
+        run(std::integral_constant<int, 1>{});
+
+    // ------------------------------------------------------------ epilogue
+    const float lt = l + __shfl_xor(l, 32);
+    if (!cvalid) return;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse_v = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+    if (p.splits == 1) {
+        T *op = (T *)p.o + (int64_t)b * p.os0 + (int64_t)tq * p.os1 + (int64_t)hq * p.os2;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                bf16x4 w;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) w[x] = (__bf16)(O[dt][4 * g4 + x] * inv);
+                *(bf16x4 *)(op + 32 * dt + 8 * g4 + 4 * hh) = w;
+            }
+        if (p.lse != nullptr && hh == 0) p.lse[((int64_t)b * p.Hq + hq) * p.Sq + tq] = lse_v;
+    } else {
+        const int64_t row = (((int64_t)sp * p.B + b) * p.Sq + tq) * p.Hq + hq;
+        float *op = p.o_part + row * D;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 w;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) w[x] = O[dt][4 * g4 + x] * inv;
+                *(f32x4 *)(op + 32 * dt + 8 * g4 + 4 * hh) = w;
+            }
+        if (hh == 0) p.lse_part[row] = lse_v;
+    }
+}
+
 // Split-KV merge.  32 threads per output row, 4 head-dim entries each.
 template <typename TO>
 __global__ __launch_bounds__(NT) void combine_kernel(const float *__restrict__ o_part,
@@ -642,8 +1129,11 @@ hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stre
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
     switch (v) {
-        case AttnVariant::BF16_WIDE:    // 8 waves, 256 columns, two bias slab buffers
-            hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 8, true>), grid, dim3(512), 0, stream, p);
+        case AttnVariant::BF16_WIDE:    // 8 waves, 256 columns
+            if (p.kv32)                 // two ping-pong groups (32-bit K/V offsets)
+                hipLaunchKernelGGL(attn_prefill_pp_kernel, grid, dim3(512), 0, stream, p);
+            else
+                hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 8, true>), grid, dim3(512), 0, stream, p);
             break;
         case AttnVariant::BF16_NARROW:  // 4 waves: 128 columns, small LDS footprint
             hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 4, false>), grid, dim3(256), 0, stream, p);

@@ -131,6 +131,8 @@ rba::AttnParams make_params(const rba_attn_args *a, const Plan &pl, int splits) 
     const int64_t ch = 16 / elem_size(a->dt);
     p.r_vec = a->R != nullptr && aligned(a->R, 16) && a->E % ch == 0 && a->R_s[0] % ch == 0 &&
               a->R_s[1] % ch == 0 && a->R_s[2] % ch == 0;
+    const int64_t kv_row = std::max(a->k_s[1], a->v_s[1]);
+    p.kv32 = ((int64_t)a->Skv * kv_row + kHeadDim) * elem_size(a->dt) < ((int64_t)1 << 31);
     return p;
 }
 

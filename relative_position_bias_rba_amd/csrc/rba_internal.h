@@ -24,6 +24,7 @@ struct AttnParams {
     int nqb;             // query blocks per (batch, kv head)
     int splits;          // key-range splits per block
     int r_vec;           // R rows allow 16-byte chunk loads
+    int kv32;            // K and V of one (batch, kv head) span less than 2^31 bytes
 };
 
 // Kernel variants.  WIDE: two 32-column tiles per wave (prefill, bf16).
