@@ -118,6 +118,16 @@ __device__ __forceinline__ void dma16(rsrc_t r, unsigned voff, void *lds_wave) {
                                              0);
 }
 
+// Maximum of a lane's value and that of lane ^ 32, without the LDS pipeline:
+// v_permlane32_swap exchanges the upper 32 lanes of one register with the
+// lower 32 lanes of the other, so with both holding x every lane ends up
+// with its own value in one register and its partner's in the other.
+__device__ __forceinline__ float max_across_halves(float x) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return fmaxf(a, b);
+}
+
 // Buffer descriptor words for dma16_untracked (same layout as make_rsrc).
 __device__ __forceinline__ u32x4 make_rsrc_words(const void *base, int64_t bytes) {
     const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
@@ -968,7 +978,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
 #pragma unroll
             for (int r = 0; r < 16; ++r) mt = fmaxf(mt, S[u][r]);
         if (!band) mt *= amul;
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = max_across_halves(mt);
         // The reference max only moves when the tile max exceeds it by more
         // than kRescaleSlack (alpha = 1 otherwise).
         const bool grow = mt > m + kRescaleSlack;
