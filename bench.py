@@ -31,6 +31,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# HBM bytes per launch of the prefill kernel: rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors
+# from a plain 1 GiB device copy under the same counters), keyed by the sha256 prefix of the kernel
+# source the counters were taken on; any other source reports null.
+PROFILED_TRAFFIC = {"1379cc7d2c513b21": 513086 * 1024 * 2 + 131079 * 1024}
+
+
+def kernel_source_hash():
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "relative_position_bias_rba_amd", "csrc",
+                        "attn_kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
 def time_events(fn, iters, torch):
     """Average duration (ms) of fn() measured with HIP events on the current stream."""
     st = torch.cuda.current_stream()
@@ -209,7 +223,8 @@ def main():
                                "(relproj + attention per step)",
                    "global_batch": w.B, "seq_len": w.Sq, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": PROFILED_TRAFFIC.get(kernel_source_hash()),
                      "kernel": "attn_prefill_pp_kernel", "avg_ms": round(ms_attn, 4),
                      "algorithmic_flops": flops},
         "kernels": {"attn_prefill_ms": round(ms_attn, 4), "attn_prefill_tflops": round(attn_tflops, 2),
