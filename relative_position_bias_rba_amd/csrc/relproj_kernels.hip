@@ -7,10 +7,13 @@
 //
 // The contraction is short (r_dim <= 128) and the output is E entries per
 // (token, head), so the kernel is bound by writing R.  A workgroup owns one
-// head and 256 tokens; it stages P[h]^T in LDS in chunks of 128 distances and
+// head, 128 tokens (32 per wave) and one chunk of up to 256 distances; it
+// stages that chunk of P[h]^T in LDS once (all loads in flight together) and
 // computes R^T tiles (32 distances x 32 tokens) with MFMA, A = P^T from LDS and
 // B = r^T from registers.  The A-operand row order makes every lane hold 16
 // consecutive distances of one token, so R is written with 16-byte stores.
+// Registers are kept low (one token tile per wave, k-steps sized to r_dim) so
+// that enough waves stay resident to keep the store stream going.
 #include "rba_internal.h"
 
 #include <type_traits>
@@ -25,21 +28,26 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NT = 256;
-constexpr int EC = 128;       // distances per LDS chunk
-constexpr int TPW = 64;       // tokens per wave (two 32-column tiles)
+constexpr int TT = 1;         // 32-token column tiles per wave
+constexpr int TPW = 32 * TT;  // tokens per wave
 constexpr int TPB = 4 * TPW;  // tokens per workgroup
 constexpr int KMAX = 128;     // largest r_dim
 
 __device__ __forceinline__ int mfma_row_key(int i) { return ((i >> 2) & 1) * 16 + (i >> 3) * 4 + (i & 3); }
 __device__ __forceinline__ int lds_row(int j) { return j ^ (((j >> 4) & 1) * 12); }
 
-template <typename TI, typename TO>
+// NK: 16-channel k-steps held in registers for bf16 input (r_dim <= 16 NK); it
+// sizes the register file use, and with it how many waves a CU keeps in flight
+// to stream the output.
+template <typename TI, typename TO, int NK>
 __global__ __launch_bounds__(NT) void relproj_kernel(const TI *__restrict__ r, int64_t rs, const TI *__restrict__ P,
-                                                     TO *__restrict__ R, int64_t T, int Hq, int r_dim, int E) {
+                                                     TO *__restrict__ R, int64_t T, int Hq, int r_dim, int E, int EC) {
     constexpr bool BF = sizeof(TI) == 2;
     constexpr int PAD = BF ? 8 : 4;
-    // P^T chunk in LDS: EC rows (distances) x KP (+pad) channels
-    __shared__ __attribute__((aligned(16))) TI sP[EC * (KMAX + PAD)];
+    // P^T chunk in LDS: EC rows (distances) x KP (+pad) channels; the workgroup's
+    // distance chunk is blockIdx.z
+    extern __shared__ __attribute__((aligned(16))) unsigned char relproj_lds[];
+    TI *sP = (TI *)relproj_lds;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, lc = lane & 31;
     const int h = blockIdx.y;
@@ -53,16 +61,16 @@ __global__ __launch_bounds__(NT) void relproj_kernel(const TI *__restrict__ r, i
     constexpr int KSTEP = BF ? 16 : 2;
     constexpr int NKS = BF ? KMAX / 16 : KMAX / 2;
     typedef typename std::conditional<BF, bf16x8, float>::type Frag;
-    Frag rf[2][BF ? 8 : 64];
+    Frag rf[TT][BF ? NK : 64];
     const int nks = BF ? KP / 16 : KP / 2;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < TT; ++c) {
         const int64_t t = tbase + 32 * c + lc;
         const bool ok = t < T;
         const TI *rp = r + (ok ? t : 0) * rs;
         if constexpr (BF) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < NK; ++k) {
                 bf16x8 x = bf16x8{};
                 const int c0 = 16 * k + 8 * hh;
                 if (ok && k < nks) {
@@ -86,41 +94,60 @@ __global__ __launch_bounds__(NT) void relproj_kernel(const TI *__restrict__ r, i
     }
     (void)NKS;
     (void)KSTEP;
+    // Settle the r loads here.  On this target stores also count in vmcnt, so
+    // a wait for these loads left inside the loop would wait for every store
+    // issued so far as well.
+#pragma unroll
+    for (int c = 0; c < TT; ++c)
+#pragma unroll
+        for (int k = 0; k < (BF ? NK : 64); ++k) asm volatile("" : "+v"(rf[c][k]));
 
     const int arow_key = mfma_row_key(lc);
-    for (int e0 = 0; e0 < E; e0 += EC) {
-        // ---- stage P[h][:, e0:e0+EC]^T: each unit = 4 channels x 8 distances
-        __syncthreads();
+    {
+        const int e0 = blockIdx.z * EC;
+        // ---- stage P[h][:, e0:e0+EC]^T: each unit = 4 channels x 8 distances.  All
+        // loads of a pass are issued before any is used (one wait per pass).
         const int units = (KP / 4) * (EC / 8);
-        for (int u = tid; u < units; u += NT) {
-            const int cq = u / (EC / 8), eq = u - cq * (EC / 8);
-            TI v[4][8];
+        constexpr int UPT = 2;   // units per thread and pass
+        for (int u0 = 0; u0 < units; u0 += UPT * NT) {
+            TI v[UPT][4][8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = 4 * cq + i;
-                const int e = e0 + 8 * eq;
-                const TI *src = P + ((int64_t)h * r_dim + c) * E + e;
-                if (c < r_dim && (E % 8 == 0) && e + 8 <= E) {
-                    if constexpr (BF) {
-                        *(u32x4 *)v[i] = *(const u32x4 *)src;
+            for (int j = 0; j < UPT; ++j) {
+                const int u = u0 + j * NT + tid;
+                const int cq = u / (EC / 8), eq = u - cq * (EC / 8);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = 4 * cq + i;
+                    const int e = e0 + 8 * eq;
+                    const TI *src = P + ((int64_t)h * r_dim + c) * E + e;
+                    if (u < units && c < r_dim && (E % 8 == 0) && e + 8 <= E) {
+                        if constexpr (BF) {
+                            *(u32x4 *)v[j][i] = *(const u32x4 *)src;
+                        } else {
+                            *(u32x4 *)&v[j][i][0] = *(const u32x4 *)src;
+                            *(u32x4 *)&v[j][i][4] = *(const u32x4 *)(src + 4);
+                        }
                     } else {
-                        *(u32x4 *)&v[i][0] = *(const u32x4 *)src;
-                        *(u32x4 *)&v[i][4] = *(const u32x4 *)(src + 4);
-                    }
-                } else {
 #pragma unroll
-                    for (int x = 0; x < 8; ++x) v[i][x] = (c < r_dim && e + x < E) ? src[x] : (TI)0.f;
+                        for (int x = 0; x < 8; ++x) v[j][i][x] = (u < units && c < r_dim && e + x < E) ? src[x] : (TI)0.f;
+                    }
                 }
             }
 #pragma unroll
+            for (int j = 0; j < UPT; ++j) {
+            const int u = u0 + j * NT + tid;
+            if (u >= units) continue;
+            const int cq = u / (EC / 8), eq = u - cq * (EC / 8);
+#pragma unroll
             for (int x = 0; x < 8; ++x) {
-                TI w[4] = {v[0][x], v[1][x], v[2][x], v[3][x]};
+                TI w[4] = {v[j][0][x], v[j][1][x], v[j][2][x], v[j][3][x]};
                 const int er = 8 * eq + x;  // distance row inside the chunk
                 TI *dst = &sP[(32 * (er >> 5) + lds_row(er & 31)) * PS + 4 * cq];
                 if constexpr (BF)
                     *(u32x2 *)dst = *(const u32x2 *)w;
                 else
                     *(u32x4 *)dst = *(const u32x4 *)w;
+            }
             }
         }
         __syncthreads();
@@ -129,15 +156,18 @@ __global__ __launch_bounds__(NT) void relproj_kernel(const TI *__restrict__ r, i
 #pragma unroll
         for (int et = 0; et < EC / 32; ++et) {
             if (e0 + 32 * et >= E) break;
-            f32x16 acc[2] = {f32x16{}, f32x16{}};
+            f32x16 acc[TT];
+#pragma unroll
+            for (int c = 0; c < TT; ++c) acc[c] = f32x16{};
             const TI *arow = &sP[(32 * et + lds_row(arow_key)) * PS];
             if constexpr (BF) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
+                for (int k = 0; k < NK; ++k) {
                     if (k < nks) {
                         const bf16x8 a = *(const bf16x8 *)(arow + 16 * k + 8 * hh);
-                        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, rf[0][k], acc[0], 0, 0, 0);
-                        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, rf[1][k], acc[1], 0, 0, 0);
+#pragma unroll
+                        for (int c = 0; c < TT; ++c)
+                            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, rf[c][k], acc[c], 0, 0, 0);
                     }
                 }
             } else {
@@ -148,8 +178,9 @@ __global__ __launch_bounds__(NT) void relproj_kernel(const TI *__restrict__ r, i
                         const f32x4 a = *(const f32x4 *)(arow + KH * hh + 4 * k4);
 #pragma unroll
                         for (int x = 0; x < 4; ++x) {
-                            acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[x], rf[0][4 * k4 + x], acc[0], 0, 0, 0);
-                            acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[x], rf[1][4 * k4 + x], acc[1], 0, 0, 0);
+#pragma unroll
+                            for (int c = 0; c < TT; ++c)
+                                acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[x], rf[c][4 * k4 + x], acc[c], 0, 0, 0);
                         }
                     }
                 }
@@ -157,7 +188,7 @@ __global__ __launch_bounds__(NT) void relproj_kernel(const TI *__restrict__ r, i
             // lane holds distances e0 + 32et + 16hh + 0..15 of token column lc
             const int eb = e0 + 32 * et + 16 * hh;
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
+            for (int c = 0; c < TT; ++c) {
                 const int64_t t = tbase + 32 * c + lc;
                 if (t >= T) continue;
                 TO *dst = R + (t * Hq + h) * (int64_t)E + eb;
@@ -196,20 +227,37 @@ hipError_t launch_relproj(bool in_bf16, bool out_bf16, int64_t T, int Hq, int r_
                           int64_t r_stride, const void *P, void *R, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     const int64_t gx = (T + TPB - 1) / TPB;
-    if (gx > 0x7fffffff || Hq > 65535) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)gx, (unsigned)Hq), block(NT);
-    if (in_bf16 && out_bf16)
-        hipLaunchKernelGGL((relproj_kernel<__bf16, __bf16>), grid, block, 0, stream, (const __bf16 *)r, r_stride,
-                           (const __bf16 *)P, (__bf16 *)R, T, Hq, r_dim, E);
-    else if (in_bf16)
-        hipLaunchKernelGGL((relproj_kernel<__bf16, float>), grid, block, 0, stream, (const __bf16 *)r, r_stride,
-                           (const __bf16 *)P, (float *)R, T, Hq, r_dim, E);
-    else if (out_bf16)
-        hipLaunchKernelGGL((relproj_kernel<float, __bf16>), grid, block, 0, stream, (const float *)r, r_stride,
-                           (const float *)P, (__bf16 *)R, T, Hq, r_dim, E);
-    else
-        hipLaunchKernelGGL((relproj_kernel<float, float>), grid, block, 0, stream, (const float *)r, r_stride,
-                           (const float *)P, (float *)R, T, Hq, r_dim, E);
+    // distances per workgroup: the largest of 256 / 128 / 64 whose P^T chunk fits 64 KiB of LDS
+    const int es = in_bf16 ? 2 : 4;
+    const int ps = ((r_dim + 15) & ~15) + (in_bf16 ? 8 : 4);
+    int EC = 256;
+    while (EC > 64 && (size_t)EC * ps * es > 65536) EC /= 2;
+    const size_t lds = (size_t)EC * ps * es;
+    const int64_t gz = (E + EC - 1) / EC;
+    if (gx > 0x7fffffff || Hq > 65535 || gz > 65535) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)gx, (unsigned)Hq, (unsigned)gz), block(NT);
+    const bool k4 = r_dim <= 64;
+    if (in_bf16 && out_bf16) {
+        if (k4)
+            hipLaunchKernelGGL((relproj_kernel<__bf16, __bf16, 4>), grid, block, lds, stream, (const __bf16 *)r,
+                               r_stride, (const __bf16 *)P, (__bf16 *)R, T, Hq, r_dim, E, EC);
+        else
+            hipLaunchKernelGGL((relproj_kernel<__bf16, __bf16, 8>), grid, block, lds, stream, (const __bf16 *)r,
+                               r_stride, (const __bf16 *)P, (__bf16 *)R, T, Hq, r_dim, E, EC);
+    } else if (in_bf16) {
+        if (k4)
+            hipLaunchKernelGGL((relproj_kernel<__bf16, float, 4>), grid, block, lds, stream, (const __bf16 *)r,
+                               r_stride, (const __bf16 *)P, (float *)R, T, Hq, r_dim, E, EC);
+        else
+            hipLaunchKernelGGL((relproj_kernel<__bf16, float, 8>), grid, block, lds, stream, (const __bf16 *)r,
+                               r_stride, (const __bf16 *)P, (float *)R, T, Hq, r_dim, E, EC);
+    } else if (out_bf16) {
+        hipLaunchKernelGGL((relproj_kernel<float, __bf16, 8>), grid, block, lds, stream, (const float *)r, r_stride,
+                           (const float *)P, (__bf16 *)R, T, Hq, r_dim, E, EC);
+    } else {
+        hipLaunchKernelGGL((relproj_kernel<float, float, 8>), grid, block, lds, stream, (const float *)r, r_stride,
+                           (const float *)P, (float *)R, T, Hq, r_dim, E, EC);
+    }
     return hipGetLastError();
 }
 

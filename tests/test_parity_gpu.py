@@ -64,6 +64,8 @@ def small(w, **over):
     (300, 5, 17, 37, torch.float32, torch.float32),
     (129, 2, 128, 200, torch.bfloat16, torch.float32),
     (1, 64, 64, 512, torch.bfloat16, torch.bfloat16),
+    (64, 3, 128, 1000, torch.bfloat16, torch.bfloat16),   # several distance chunks, ragged last one
+    (40, 2, 128, 130, torch.float32, torch.float32),      # the smallest chunk size
 ])
 def test_relproj_parity(T, Hq, r_dim, E, dt, odt):
     say(f"relproj T={T} Hq={Hq} r_dim={r_dim} E={E} {dt}->{odt}")
