@@ -1097,27 +1097,66 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     }
 }
 
-// Split-KV merge.  32 threads per output row, 4 head-dim entries each.
-template <typename TO>
+// Split-KV merge.  32 lanes cover one output row (4 head-dim entries each);
+// SG groups of 32 lanes share a row and each merge every SG-th split, then
+// the groups' partial (max, sum, weighted output) are merged through LDS.
+// SG = 8 serves few rows with many splits (long-context decode), SG = 1 many
+// rows with few splits.
+template <typename TO, int SG>
 __global__ __launch_bounds__(NT) void combine_kernel(const float *__restrict__ o_part,
                                                      const float *__restrict__ lse_part, int splits, int B, int Sq,
                                                      int Hq, TO *__restrict__ o, int64_t os0, int64_t os1,
                                                      int64_t os2, float *__restrict__ lse) {
+    constexpr int RPB = NT / 32 / SG;   // rows per block
+    __shared__ float part[SG > 1 ? NT / 32 : 1][2 + 32 * 4];
     const int64_t rows = (int64_t)B * Sq * Hq;
-    const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+    const int g32 = threadIdx.x >> 5;   // 32-lane group
+    const int grp = g32 % SG;           // split group of the row
+    const int64_t row = (int64_t)blockIdx.x * RPB + g32 / SG;
     const int c = threadIdx.x & 31;
-    if (row >= rows) return;
+    const bool live = row < rows;
     float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, lse_part[s * rows + row]);
+    if (live) {
+#pragma unroll 4
+        for (int s = grp; s < splits; s += SG) M = fmaxf(M, lse_part[s * rows + row]);
+    }
     const float Ms = M == -INFINITY ? 0.f : M;
     f32x4 acc = f32x4{};
     float den = 0.f;
-    for (int s = 0; s < splits; ++s) {
-        const float w = fast_exp2((lse_part[s * rows + row] - Ms) * kLog2e);
-        den += w;
-        const f32x4 x = *(const f32x4 *)(o_part + (s * rows + row) * D + 4 * c);
-        acc += w * x;
+    if (live) {
+#pragma unroll 4
+        for (int s = grp; s < splits; s += SG) {
+            const float w = fast_exp2((lse_part[s * rows + row] - Ms) * kLog2e);
+            den += w;
+            const f32x4 x = *(const f32x4 *)(o_part + (s * rows + row) * D + 4 * c);
+            acc += w * x;
+        }
     }
+    float Mt = M;
+    if constexpr (SG > 1) {
+        float *mine = part[g32];
+        if (c == 0) {
+            mine[0] = M;
+            mine[1] = den;
+        }
+        *(f32x4 *)&mine[2 + 4 * c] = acc;
+        __syncthreads();
+        if (grp != 0) return;
+        Mt = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < SG; ++g) Mt = fmaxf(Mt, part[g32 + g][0]);
+        acc = f32x4{};
+        den = 0.f;
+#pragma unroll
+        for (int g = 0; g < SG; ++g) {
+            const float *pg = part[g32 + g];
+            const float w = pg[0] == -INFINITY ? 0.f : fast_exp2((pg[0] - Mt) * kLog2e);
+            den += w * pg[1];
+            acc += w * *(const f32x4 *)&pg[2 + 4 * c];
+        }
+    }
+    if (!live) return;
+    const float Mf = Mt == -INFINITY ? 0.f : Mt;
     const float inv = den > 0.f ? 1.f / den : 0.f;
     const int h = (int)(row % Hq);
     const int64_t bt = row / Hq;
@@ -1126,7 +1165,7 @@ __global__ __launch_bounds__(NT) void combine_kernel(const float *__restrict__ o
     TO *op = o + (int64_t)b * os0 + (int64_t)t * os1 + (int64_t)h * os2 + 4 * c;
 #pragma unroll
     for (int x = 0; x < 4; ++x) op[x] = (TO)(acc[x] * inv);
-    if (lse != nullptr && c == 0) lse[((int64_t)b * Hq + h) * Sq + t] = den > 0.f ? Ms + logf(den) : -INFINITY;
+    if (lse != nullptr && c == 0) lse[((int64_t)b * Hq + h) * Sq + t] = den > 0.f ? Mf + logf(den) : -INFINITY;
 }
 
 }  // namespace
@@ -1159,13 +1198,26 @@ hipError_t launch_combine(const float *o_part, const float *lse_part, int splits
                           bool o_bf16, int64_t os0, int64_t os1, int64_t os2, float *lse, hipStream_t stream) {
     const int64_t rows = (int64_t)B * Sq * Hq;
     if (rows <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((rows + 7) / 8)), block(NT);
-    if (o_bf16)
-        hipLaunchKernelGGL((combine_kernel<__bf16>), grid, block, 0, stream, o_part, lse_part, splits, B, Sq, Hq,
-                           (__bf16 *)o, os0, os1, os2, lse);
-    else
-        hipLaunchKernelGGL((combine_kernel<float>), grid, block, 0, stream, o_part, lse_part, splits, B, Sq, Hq,
-                           (float *)o, os0, os1, os2, lse);
+    // few rows: one row per block, the splits spread over 8 lane groups
+    const bool wide = rows < 8192 && splits >= 8;
+    const int64_t blocks = wide ? rows : (rows + 7) / 8;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)blocks), block(NT);
+    if (o_bf16) {
+        if (wide)
+            hipLaunchKernelGGL((combine_kernel<__bf16, 8>), grid, block, 0, stream, o_part, lse_part, splits, B, Sq, Hq,
+                               (__bf16 *)o, os0, os1, os2, lse);
+        else
+            hipLaunchKernelGGL((combine_kernel<__bf16, 1>), grid, block, 0, stream, o_part, lse_part, splits, B, Sq, Hq,
+                               (__bf16 *)o, os0, os1, os2, lse);
+    } else {
+        if (wide)
+            hipLaunchKernelGGL((combine_kernel<float, 8>), grid, block, 0, stream, o_part, lse_part, splits, B, Sq, Hq,
+                               (float *)o, os0, os1, os2, lse);
+        else
+            hipLaunchKernelGGL((combine_kernel<float, 1>), grid, block, 0, stream, o_part, lse_part, splits, B, Sq, Hq,
+                               (float *)o, os0, os1, os2, lse);
+    }
     return hipGetLastError();
 }
 

@@ -207,14 +207,20 @@ def test_decode_split_invariance_and_prefill_agreement():
 
 # --------------------------------------------------------------------------- combine kernel on its own
 
-def test_combine_kernel_parity():
+@pytest.mark.parametrize("S,B,Sq,Hq", [
+    (6, 2, 3, 8),        # many rows, few splits: one lane group per row
+    (64, 1, 1, 64),      # few rows, many splits: the splits spread over lane groups of a row
+    (13, 1, 2, 5),       # few rows, split count not a multiple of the group count
+])
+def test_combine_kernel_parity(S, B, Sq, Hq):
+    say(f"combine S={S} B={B} Sq={Sq} Hq={Hq}")
     m = rba()
-    g = torch.Generator().manual_seed(5)
-    S, B, Sq, Hq = 6, 2, 3, 8
+    g = torch.Generator().manual_seed(5 + S)
     op = torch.randn(S, B, Sq, Hq, 128, generator=g)
     lp = torch.randn(S, B, Sq, Hq, generator=g) * 3
     lp[1, 0] = -math.inf            # an empty split for some rows
-    lp[:, 1, 2, 5] = -math.inf      # a row with no visible key at all
+    lp[:, B - 1, Sq - 1, Hq - 1] = -math.inf   # a row with no visible key at all
+    lp[0:8, 0, 0, 0] = -math.inf    # a whole lane group's share of one row empty
     q_like = torch.empty(B, Sq, Hq, 128, dtype=torch.float32, device=DEV)
     k_like = torch.empty(B, Sq, 1, 128, dtype=torch.float32, device=DEV)
     o, lse = m.splitkv_combine(op.to(DEV), lp.to(DEV), q_like, k_like, return_lse=True)
