@@ -646,9 +646,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 //   group 0: phase 2t   MFMA [PV(t-1), QK(t)]   phase 2t+1 VALU [softmax(t)]
 //   group 1: phase 2t   VALU [softmax(t-1)]     phase 2t+1 MFMA [PV(t-1), QK(t)]
 // Each group runs its own copy of the phase loop with its roles fixed at
-// compile time.  All staging is global -> LDS DMA issued by group 0 between
-// the matrix instructions of its even phases and awaited at the end of the
-// following odd phase: K(t+1), V(t) and the bias windows of both groups
+// compile time.  All staging is global -> LDS DMA issued by group 1 in bursts
+// between the parts of its even-phase softmax (the matrix group's phase is the
+// longer one) and awaited at the end of the following odd phase: K(t+1), V(t) and the bias windows of both groups
 // (group 0's for tile t+1, group 1's for tile t).  V is kept row-major in LDS
 // (16-byte chunks XOR-swizzled by row) and read as the PV A-operand with the
 // LDS transpose read, so it never passes through registers.  LDS regions are
@@ -752,7 +752,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
 #pragma unroll
     for (int i = 0; i < 2 * KT; ++i) P[i] = bf16x8{};
 
-    // ------------------------------------------------------------ staging offsets (group 0 lanes)
+    // ------------------------------------------------------------ staging offsets (lanes of the issuing group)
     // K: LDS chunk L holds chunk L % CPRP of key row lds_key_row(L / CPRP);
     // the padding chunk reloads chunk 0.  Chunks past the tile land in the
     // padding of the buffer.
@@ -942,7 +942,17 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     };
     // Vector phase: bias, mask, running max and exponentials of tile t
     // (sequence index), key tile kt.
-    auto softmax = [&](int t, int kt) __attribute__((always_inline)) {
+    // With DMA the group issues this phase's staging instructions in four
+    // bursts spread over the softmax.
+    auto softmax = [&](int t, int kt, auto dma_c) __attribute__((always_inline)) {
+        constexpr bool DMA = decltype(dma_c)::value;
+        auto burst = [&](int s0, int s1) __attribute__((always_inline)) {
+            if constexpr (DMA) {
+#pragma unroll
+                for (int s = s0; s < s1; ++s) issue(s);
+            }
+        };
+        burst(0, 6);
         const int j0 = kt * N;
         const bool band = banded(kt);
         const bool edge = !((j0 + N - 1 <= p_min) && (W == 0 || p_max - j0 < W));
@@ -977,6 +987,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
         for (int u = 0; u < KT; ++u)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mt = fmaxf(mt, S[u][r]);
+        burst(6, 11);
         if (!band) mt *= amul;
         mt = max_across_halves(mt);
         // The reference max only moves when the tile max exceeds it by more
@@ -1002,6 +1013,8 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
                     sum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[2 * x], pb[2 * x + 1]},
                                                           bf16x2{(__bf16)1.f, (__bf16)1.f}, sum, false);
                 P[2 * u + h2] = pb;
+                if (u == 0 && h2 == 0) burst(11, 15);
+                if (u == 0 && h2 == 1) burst(15, NSLOT);
             }
         l += sum;
     };
@@ -1040,21 +1053,28 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
             }
             // even phase
             if constexpr (G == 0) {
-                plan_even(t, w1, w2);
                 // P is zero before the first softmax (PV then adds nothing;
                 // V buffer 0 holds the first tile); the QK after the last
                 // tile is never used.
-                mfma_phase(t >= 1 ? t - 1 : 0, t, std::true_type{});
+                mfma_phase(t >= 1 ? t - 1 : 0, t, std::false_type{});
             } else {
-                if (wave_active && t >= 1) softmax(t - 1, w0);
+                // group 1 stages the tiles of this even phase while it runs
+                // its softmax (the matrix group's phase is the longer one)
+                plan_even(t, w1, w2);
+                if (wave_active && t >= 1) {
+                    softmax(t - 1, w0, std::true_type{});
+                } else {
+#pragma unroll
+                    for (int s = 0; s < NSLOT; ++s) issue(s);
+                }
             }
             lds_barrier();
             // odd phase
             if constexpr (G == 0) {
-                if (t < n_it) softmax(t, w1);
-                wait_vmem();      // staging of the even phase has landed
+                if (t < n_it) softmax(t, w1, std::false_type{});
             } else {
                 if (wave_active) mfma_phase(t >= 1 ? t - 1 : 0, t, std::false_type{});
+                wait_vmem();      // staging of the even phase has landed
             }
             lds_barrier();
         }
