@@ -125,6 +125,8 @@ PREFILL_CASES = [
     ("sq_lt_skv", dict(B=2, Sq=77, Skv=333, Hq=16, Hkv=2, window=128, E=64, log_scale_base=64.0)),
     ("window1", dict(B=1, Sq=130, Skv=130, Hq=8, Hkv=1, window=1, E=16)),
     ("tiny", dict(B=1, Sq=1, Skv=1, Hq=8, Hkv=1, window=0, E=8)),
+    ("wide_partial", dict(B=2, Sq=20, Skv=150, Hq=8, Hkv=1, window=0, E=64)),   # 160 of 256 columns
+    ("gqa12", dict(B=1, Sq=100, Skv=100, Hq=24, Hkv=2, window=40, E=64)),      # 12 heads x 21 rows
 ]
 
 
@@ -137,6 +139,31 @@ def test_prefill_bf16_small(name, over):
     wo, wl = oracle_full(inp, w)
     check(f"{name} o", o, wo, False)
     check(f"{name} lse", lse, wl, True, extra_tol=2e-2)
+
+
+def test_prefill_kv_spans_beyond_31_bits():
+    """K and V rows 8 MiB apart (each tensor spans more than 2^31 bytes): the
+    prefill takes its 64-bit-offset path; results as for dense K and V."""
+    m = rba()
+    w = small(CONFIGS["c2_swa_prefill"], B=1, Sq=300, Skv=300, Hq=16, Hkv=2, window=96, E=64)
+    say(f"prefill with 8 MiB K/V row stride: {w}")
+    inp = make_inputs(w)
+    d = to_dev(inp)
+    rs = 1 << 22                      # elements between consecutive key rows
+    kv = []
+    for name in ("k", "v"):
+        buf = torch.empty(w.Skv * rs, dtype=torch.bfloat16, device=DEV)
+        view = buf.as_strided((w.B, w.Skv, w.Hkv, w.d), (w.Skv * rs, rs, w.d, 1))
+        view.copy_(d[name])
+        kv.append(view)
+    R = m.relproj(d["r"], d["P"])
+    o, lse = m.attn_prefill(d["q"], kv[0], kv[1], R, window=w.window, return_lse=True)
+    torch.cuda.synchronize()
+    wo, wl = oracle_full(inp, w)
+    check("large-stride o", o, wo, False)
+    check("large-stride lse", lse, wl, True, extra_tol=2e-2)
+    del kv, buf
+    torch.cuda.empty_cache()
 
 
 def test_prefill_fp32_variants():
