@@ -247,6 +247,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
                 qf[4 * k + 3] = x[3];
             }
         }
+        // Settle the loads here.  vmcnt counts in order, so a wait for them
+        // left inside the tile loop would also wait for the next tile's V loads
+        // (the wait there is then for the K tile only, the one the compiler
+        // keeps ahead of the LDS reads).
+#pragma unroll
+        for (int k = 0; k < QREGS; ++k) asm volatile("" : "+v"(qf[k]));
     }
 
     f32x16 O[4];
