@@ -291,10 +291,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     const bool r_dma = has_bias && p.r_vec;
     unsigned svo[NSI];
     rsrc_t rR;
+    u32x4 rR4;
     {
         const int64_t rbase = (int64_t)b * p.Rs0 + (int64_t)t0 * p.Rs1 + (int64_t)hkv * p.G * p.Rs2;
         const int64_t rspan = ((int64_t)(nrows - 1) * p.Rs1 + (int64_t)(p.G - 1) * p.Rs2 + p.E) * ES;
         rR = make_rsrc(has_bias ? (const T *)p.R + rbase : (const T *)p.q, has_bias ? rspan : 0);
+        rR4 = make_rsrc_words(has_bias ? (const T *)p.R + rbase : (const T *)p.q, has_bias ? rspan : 0);
 #pragma unroll
         for (int i = 0; i < NSI; ++i) {
             const int L = (i * NW + wave) * 64 + lane;
@@ -393,6 +395,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
                     *(u32x4 *)&sR[buf][L * CH] = val;
                 }
             }
+        }
+    };
+
+    // The single bias buffer (SLAB2 false) for key tile kt, issued while the
+    // tile before it is computed (that tile then carries no bias, so the
+    // buffer is free).  Untracked so that the compiler does not hold the LDS
+    // reads of that compute until it lands; the end-of-iteration wait does.
+    auto stage_slab_ahead = [&](int kt) {
+        const unsigned eoff = (unsigned)(-kt * N * ES);
+#pragma unroll
+        for (int i = 0; i < NSI; ++i) {
+            const int wc = (i * NW + wave) * 64;
+            if (i < NSI - 1 || wc + lane < SCH) dma16_untracked(rR4, svo[i] + eoff, &sR[0][wc * CH]);
         }
     };
 
@@ -582,8 +597,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         const int cur = it & 1;
         const bool nxt = it + 1 < n_it;
         const int kn = nxt ? next_tile() : kt;
+        const bool slab_ahead = !SLAB2 && nxt && r_dma && banded(kn) && !banded(kt);
         if (nxt) {
             stage_k(kn, cur ^ 1);
+            if (slab_ahead) stage_slab_ahead(kn);
             load_v(kn);
             if (SLAB2 && banded(kn)) stage_slab(kn, cur ^ 1);
         }
@@ -592,7 +609,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         __syncthreads();             // tile kt fully consumed; loads for kn landed
         if (nxt) {
             store_v();
-            if (!SLAB2 && banded(kn)) {
+            if (!SLAB2 && banded(kn) && !slab_ahead) {
                 stage_slab(kn, 0);
                 wait_vmem();
             }
