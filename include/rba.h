@@ -16,6 +16,11 @@
  *            size 128; the relative term is added before softmax.
  *   [V-OPT]  same page, section "低レイテンシコレクティブとカーネル": the
  *            split-KV factor (num_splits) is chosen per batch size and KV length.
+ *   [V-KV]   same page, section "vLLM テクニカル最適化": the serving engine keeps
+ *            the caches of all layers in one unified KV cache manager, and
+ *            multi-token prediction re-runs its heads over the accepted
+ *            tokens; read here as sequences of their own lengths whose keys
+ *            are reached through a table of fixed-size pages.
  *
  * For batch b, query head h (kv head g = h / (Hq/Hkv)), query row t at
  * position p = Skv - Sq + t, and key j:
@@ -114,6 +119,40 @@ size_t rba_decode_workspace_bytes(const rba_attn_args *args, int num_splits);
  * Returns RBA_E_WORKSPACE if workspace is NULL or too small when needed.   */
 rba_status rba_attn_decode(const rba_attn_args *args, int num_splits, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/* Paged, variable-length K/V for rba_attn_paged ([V-KV]).  The cache is a
+ * pool of pages of page_size consecutive keys of every kv head:
+ *   args->k, args->v : [num_pages][page_size][Hkv][d]  strides k_s / v_s =
+ *                      {page, key, head} (elements)
+ * Sequence b has seq_lens[b] keys; key j of it is row j % page_size of page
+ * block_table[b * bt_stride + j / page_size].  Its Sq query rows are its last
+ * Sq positions: query row t sits at position seq_lens[b] - Sq + t.
+ *   block_table : device int32 [B][bt_stride]; entries outside [0, num_pages)
+ *                 are clamped into it on the device (never read out of bounds)
+ *   seq_lens    : device int32 [B]; a length outside [Sq, args->Skv] is
+ *                 clamped into it on the device.  args->Skv is the longest
+ *                 length the table covers and drives the split heuristic.
+ *   page_size   : a positive multiple of 64 (a page holds whole key tiles)
+ *   bt_stride   : >= ceil(args->Skv / page_size)
+ * The host cannot check device-side values; a table that names pages the
+ * caller did not fill yields their contents, not an error.                 */
+typedef struct rba_paged_kv {
+    const int32_t *block_table;
+    const int32_t *seq_lens;
+    int64_t bt_stride;
+    int page_size;
+    int num_pages;
+} rba_paged_kv;
+
+/* Attention of each sequence's last Sq query rows over its own paged keys
+ * ([V-KV], [S-RPB]); the same logits, mask, bias and outputs as
+ * rba_attn_decode (q, o, R and lse keep their [B, Sq, ...] layouts and the
+ * same workspace rules and size, rba_decode_workspace_bytes(args, splits)).
+ * num_splits = 0 uses rba_num_splits(args): splits then cover each
+ * sequence's own key range.  Also serves chunked prefill and multi-token
+ * verification (Sq > 1) over a paged cache.                                */
+rba_status rba_attn_paged(const rba_attn_args *args, const rba_paged_kv *kv, int num_splits, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /* Merge split partials into args->o (and args->lse if non-NULL):
  *   M = max_s lse_s;  w_s = exp(lse_s - M);  o = sum_s w_s o_s / sum_s w_s;

@@ -23,6 +23,9 @@ prose only; no listing, worked example or numbers exist for this path):
   [V-ARCH] "vLLM TML Inkling サポート" (agentlenshq.com), section
            "TML Inkling モデルアーキテクチャ": GQA with head size 128 in every
            layer; the relative term is added to the logits before softmax.
+  [V-KV]   same page, section "vLLM テクニカル最適化": the serving engine
+           keeps the caches of all layers in one unified KV cache manager and
+           re-runs the multi-token-prediction heads over accepted tokens.
 
 Readings taken where the pages leave a step open (each is one line in the
 design notes):
@@ -36,13 +39,18 @@ design notes):
   * Window W > 0: key j visible iff 0 <= p-j < W.  W = 0: full causal.
   * Query row t sits at position p = Skv - Sq + t.
   * GQA: query head h reads kv head h // (Hq/Hkv).
+  * Paged cache ([V-KV]): sequence b has its own length L_b; its key j is row
+    j % page_size of page block_table[b][j // page_size] of a shared pool;
+    its Sq query rows are its last Sq positions, L_b - Sq + t.
 
 Pins (tests/test_oracle.py): brute force on tiny shapes; R = 0 against
 torch's scaled_dot_product_attention in fp64; closed forms for uniform
 weights (mean of visible v, lse = ln n), single visible key, one-hot bias
 with position-coded v, shift invariance when W <= E, and the log-scale factor
 through a two-level closed form.  The LSE combine is pinned by splitting a
-full oracle result over key ranges and recombining.
+full oracle result over key ranges and recombining.  Paged attention is
+pinned by brute force on a hand-built page layout, by a permuted pool equal
+to the dense result, and by invariance under relabelling the pages.
 """
 from __future__ import annotations
 
@@ -58,6 +66,8 @@ __all__ = [
     "attention_partial",
     "lse_combine",
     "brute_attention",
+    "gather_pages",
+    "attention_paged",
 ]
 
 
@@ -286,4 +296,42 @@ def brute_attention(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0
                 for c in range(d):
                     o[b, t, h, c] = sum(math.exp(x - m) * v[b, j, g, c] for j, x in logits) / den
                 lse[b, h, t] = m + math.log(den)
+    return o, lse
+
+
+def gather_pages(pool, table_row, length):
+    """Keys 0 .. length-1 of one sequence from a paged pool ([V-KV] reading):
+    key j is row j % page_size of page table_row[j // page_size].
+    pool [num_pages, page_size, Hkv, d] -> [length, Hkv, d] (fp64)."""
+    table_row = np.asarray(table_row, dtype=np.int64)
+    ps = pool.shape[1]
+    j = np.arange(int(length))
+    return _f64(pool[table_row[j // ps], j % ps])   # pick the rows, then upcast them
+
+
+def attention_paged(q, k_pool, v_pool, block_table, seq_lens, R=None, *, window=0, scale=None,
+                    log_scale_base=0.0):
+    """Attention of each sequence's last Sq query rows over its own paged keys.
+
+    q [B,Sq,Hq,d]; k_pool/v_pool [num_pages, page_size, Hkv, d];
+    block_table [B, n_max] page indices; seq_lens [B] with Sq <= L_b.
+    Sequence b is the dense problem over keys gather_pages(pool, table[b], L_b),
+    its query row t at position L_b - Sq + t.  Returns o [B,Sq,Hq,d] and
+    lse [B,Hq,Sq] like ``attention``.
+    """
+    q = _f64(q)
+    R = _f64(R)
+    B, Sq, Hq, d = q.shape
+    o = np.zeros((B, Sq, Hq, d))
+    lse = np.zeros((B, Hq, Sq))
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L < Sq:
+            raise ValueError("a sequence must hold its own query rows")
+        Kb = gather_pages(k_pool, block_table[b], L)[None]
+        Vb = gather_pages(v_pool, block_table[b], L)[None]
+        ob, lb = attention(q[b:b + 1], Kb, Vb, None if R is None else R[b:b + 1], window=window,
+                           scale=scale, log_scale_base=log_scale_base)
+        o[b] = ob[0]
+        lse[b] = lb[0]
     return o, lse

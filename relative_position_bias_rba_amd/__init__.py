@@ -19,7 +19,7 @@ import os
 import torch
 
 __all__ = [
-    "relproj", "attn_prefill", "attn_decode", "splitkv_combine", "num_splits",
+    "relproj", "attn_prefill", "attn_decode", "attn_paged", "splitkv_combine", "num_splits",
     "decode_workspace_bytes", "lib_path", "RBAError",
     "RBA_OK", "RBA_E_INVALID", "RBA_E_UNSUPPORTED", "RBA_E_WORKSPACE", "RBA_E_LAUNCH",
 ]
@@ -54,6 +54,16 @@ class _AttnArgs(ctypes.Structure):
     ]
 
 
+class _PagedKV(ctypes.Structure):
+    _fields_ = [
+        ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("bt_stride", ctypes.c_int64),
+        ("page_size", ctypes.c_int),
+        ("num_pages", ctypes.c_int),
+    ]
+
+
 def _load():
     if not os.path.exists(lib_path):
         raise ImportError(
@@ -72,6 +82,8 @@ def _load():
     lib.rba_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.rba_attn_decode.argtypes = [P, ci, vp, ctypes.c_size_t, vp]
     lib.rba_attn_decode.restype = ci
+    lib.rba_attn_paged.argtypes = [P, ctypes.POINTER(_PagedKV), ci, vp, ctypes.c_size_t, vp]
+    lib.rba_attn_paged.restype = ci
     lib.rba_splitkv_combine.argtypes = [vp, vp, ci, P, vp]
     lib.rba_splitkv_combine.restype = ci
     lib.rba_status_string.argtypes = [ci]
@@ -197,6 +209,56 @@ def attn_decode(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0, nu
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     code = _lib.rba_attn_decode(ctypes.byref(a), splits, ws_ptr, ws_bytes, _stream(q.device))
     _check("rba_attn_decode", code)
+    return (o, lse) if return_lse else o
+
+
+def make_paged(block_table, seq_lens, page_size: int, num_pages: int) -> _PagedKV:
+    """Fill the C paged-cache struct (pointers and sizes only)."""
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [B, n] with contiguous rows")
+    kv = _PagedKV()
+    kv.block_table = block_table.data_ptr()
+    kv.seq_lens = seq_lens.data_ptr()
+    kv.bt_stride = block_table.stride(0)
+    kv.page_size = int(page_size)
+    kv.num_pages = int(num_pages)
+    return kv
+
+
+def attn_paged(q, k_pool, v_pool, block_table, seq_lens, R=None, *, max_seq_len=None, window=0, scale=None,
+               log_scale_base=0.0, num_splits=0, return_lse=False, out=None, workspace=None):
+    """Attention of each sequence's last Sq query rows over its own keys in a
+    paged pool k_pool / v_pool [num_pages, page_size, Hkv, 128].
+
+    block_table int32 [B, n] (device) lists each sequence's pages; seq_lens
+    int32 [B] (device) its key count.  max_seq_len (default n * page_size)
+    bounds seq_lens and drives the split heuristic."""
+    _check_attn_inputs(q, k_pool, v_pool, R)
+    if not (block_table.is_cuda and seq_lens.is_cuda):
+        raise ValueError("block_table and seq_lens must live on the GPU")
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    lse = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=q.device) \
+        if return_lse else None
+    num_pages, page_size = k_pool.shape[0], k_pool.shape[1]
+    if v_pool.shape[:2] != k_pool.shape[:2]:
+        raise ValueError("k_pool and v_pool must have the same pages")
+    a = make_args(q, k_pool, v_pool, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base)
+    a.Skv = int(block_table.shape[1] * page_size if max_seq_len is None else max_seq_len)
+    kv = make_paged(block_table, seq_lens, page_size, num_pages)
+    splits = int(num_splits)
+    if splits == 0:
+        splits = _lib.rba_num_splits(ctypes.byref(a), 0)
+        if splits <= 0:
+            _check("rba_num_splits", RBA_E_INVALID)
+    need = _lib.rba_decode_workspace_bytes(ctypes.byref(a), splits)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = _lib.rba_attn_paged(ctypes.byref(a), ctypes.byref(kv), splits, ws_ptr, ws_bytes, _stream(q.device))
+    _check("rba_attn_paged", code)
     return (o, lse) if return_lse else o
 
 

@@ -147,7 +147,10 @@ __device__ __forceinline__ void dma16_untracked(u32x4 rsrc, unsigned voff, const
                  : "memory", "m0");
 }
 
-template <typename T, int NW, bool SLAB2>
+// PG: K and V live in a pool of fixed-size pages; key tile kt of sequence b
+// is read from page block_table[b][kt * N / page_size] (a page holds whole
+// tiles), and sequence b has its own length seq_lens[b].
+template <typename T, int NW, bool SLAB2, bool PG>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnParams p) {
     using TL = Tile<T>;
     constexpr bool BF = sizeof(T) == 2;
@@ -194,7 +197,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     const int hkv = bh - b * p.Hkv;
     const int t0 = qb * p.QB;
     const int nrows = min(p.QB, p.Sq - t0);
-    const int pos0 = p.Skv - p.Sq;
+    // keys of this sequence; a paged length outside [Sq, Skv] is clamped
+    const int Skv = PG ? min(max(p.seq_lens[b], p.Sq), p.Skv) : p.Skv;
+    const int pos0 = Skv - p.Sq;
     const int p_min = pos0 + t0;
     const int p_max = p_min + nrows - 1;
     const int W = p.window;
@@ -206,8 +211,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     const int ncols = p.G * p.QB;
     const bool has_bias = p.R != nullptr && p.E > 0;
 
-    const T *__restrict__ gk = (const T *)p.k + (int64_t)b * p.ks0 + (int64_t)hkv * p.ks2;
-    const T *__restrict__ gv = (const T *)p.v + (int64_t)b * p.vs0 + (int64_t)hkv * p.vs2;
+    // paged: the page offset is added per tile
+    const T *__restrict__ gk = (const T *)p.k + (PG ? 0 : (int64_t)b * p.ks0) + (int64_t)hkv * p.ks2;
+    const T *__restrict__ gv = (const T *)p.v + (PG ? 0 : (int64_t)b * p.vs0) + (int64_t)hkv * p.vs2;
 
     // ------------------------------------------------------------ this lane's query column
     const int col = wave * 32 + lc;
@@ -315,12 +321,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 
     auto banded = [&](int kt) { return has_bias && (p_min - (kt * N + N - 1) < p.E); };
 
-    auto kv_rsrc = [&](const T *g, int64_t stride, int j0) {
-        return make_rsrc(g + (int64_t)j0 * stride, ((int64_t)(p.Skv - 1 - j0) * stride + D) * ES);
+    // Rows j0 .. of K or V; rows past the sequence (or the page) read zeros.
+    auto kv_rsrc = [&](const T *g, int64_t pstride, int64_t stride, int j0) {
+        if constexpr (PG) {
+            const int pg = j0 / p.page_size;
+            const int off = j0 - pg * p.page_size;
+            const int page = min(max(p.block_table[(int64_t)b * p.bt_stride + pg], 0), p.num_pages - 1);
+            const int rows = min(p.page_size - off, Skv - j0);
+            return make_rsrc(g + (int64_t)page * pstride + (int64_t)off * stride,
+                             ((int64_t)(rows - 1) * stride + D) * ES);
+        } else {
+            return make_rsrc(g + (int64_t)j0 * stride, ((int64_t)(Skv - 1 - j0) * stride + D) * ES);
+        }
     };
 
     auto stage_k = [&](int kt, int buf) {
-        const rsrc_t rk = kv_rsrc(gk, p.ks1, kt * N);
+        const rsrc_t rk = kv_rsrc(gk, p.ks0, p.ks1, kt * N);
 #pragma unroll
         for (int i = 0; i < NKI; ++i) {
             const int wc = (i * NW + wave) * 64;
@@ -329,7 +345,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     };
 
     auto load_v = [&](int kt) {
-        const rsrc_t rv = kv_rsrc(gv, p.vs1, kt * N);
+        const rsrc_t rv = kv_rsrc(gv, p.vs0, p.vs1, kt * N);
 #pragma unroll
         for (int i = 0; i < NVI; ++i) {
             if constexpr (BF)
@@ -1220,18 +1236,27 @@ hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stre
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
+    const bool paged = p.block_table != nullptr;
     switch (v) {
         case AttnVariant::BF16_WIDE:    // 8 waves, 256 columns
-            if (p.kv32)                 // two ping-pong groups (32-bit K/V offsets)
+            if (paged)
+                hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 8, true, true>), grid, dim3(512), 0, stream, p);
+            else if (p.kv32)            // two ping-pong groups (32-bit K/V offsets)
                 hipLaunchKernelGGL(attn_prefill_pp_kernel, grid, dim3(512), 0, stream, p);
             else
-                hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 8, true>), grid, dim3(512), 0, stream, p);
+                hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 8, true, false>), grid, dim3(512), 0, stream, p);
             break;
         case AttnVariant::BF16_NARROW:  // 4 waves: 128 columns, small LDS footprint
-            hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 4, false>), grid, dim3(256), 0, stream, p);
+            if (paged)
+                hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 4, false, true>), grid, dim3(256), 0, stream, p);
+            else
+                hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 4, false, false>), grid, dim3(256), 0, stream, p);
             break;
         case AttnVariant::FP32:
-            hipLaunchKernelGGL((attn_fwd_kernel<float, 4, false>), grid, dim3(256), 0, stream, p);
+            if (paged)
+                hipLaunchKernelGGL((attn_fwd_kernel<float, 4, false, true>), grid, dim3(256), 0, stream, p);
+            else
+                hipLaunchKernelGGL((attn_fwd_kernel<float, 4, false, false>), grid, dim3(256), 0, stream, p);
             break;
     }
     return hipGetLastError();

@@ -15,6 +15,7 @@ namespace {
 constexpr int kHeadDim = 128;
 constexpr int kMaxSplits = 1024;
 constexpr int kMinTilesPerSplit = 4;
+constexpr int kPageQuantum = 64;   // paged K/V: a page holds whole 64-key tiles
 
 int elem_size(rba_dtype dt) { return dt == RBA_BF16 ? 2 : 4; }
 
@@ -204,6 +205,47 @@ rba_status rba_attn_decode(const rba_attn_args *args, int num_splits, void *work
     const size_t need = workspace_bytes(args, num_splits);
     if (workspace == nullptr || workspace_bytes_ < need || !aligned(workspace, 16)) return RBA_E_WORKSPACE;
     rba::AttnParams p = make_params(args, pl, num_splits);
+    const size_t rows = (size_t)args->B * args->Sq * args->Hq;
+    p.o_part = (float *)workspace;
+    p.lse_part = p.o_part + (size_t)num_splits * rows * kHeadDim;
+    if (rba::launch_attention(p, pl.var, s) != hipSuccess) return RBA_E_LAUNCH;
+    return rba_splitkv_combine(p.o_part, p.lse_part, num_splits, args, stream);
+}
+
+rba_status rba_attn_paged(const rba_attn_args *args, const rba_paged_kv *kv, int num_splits, void *workspace,
+                          size_t workspace_bytes_, void *stream) {
+    const rba_status st = validate_attn(args);
+    if (st != RBA_OK) return st;
+    if (kv == nullptr) return RBA_E_INVALID;
+    if (num_splits < 0 || num_splits > kMaxSplits) return RBA_E_INVALID;
+    if (kv->page_size < kPageQuantum || kv->page_size % kPageQuantum != 0 || kv->num_pages < 1)
+        return RBA_E_INVALID;
+    if (kv->bt_stride < ((int64_t)args->Skv + kv->page_size - 1) / kv->page_size) return RBA_E_INVALID;
+    if ((int64_t)args->B * args->Sq == 0) return RBA_OK;
+    if (kv->block_table == nullptr || kv->seq_lens == nullptr || !aligned(kv->block_table, 4) ||
+        !aligned(kv->seq_lens, 4))
+        return RBA_E_INVALID;
+    // one page of K or V must lie within a 32-bit buffer range
+    const int64_t kv_row = std::max(args->k_s[1], args->v_s[1]);
+    if (((int64_t)(kv->page_size - 1) * kv_row + kHeadDim) * elem_size(args->dt) >= ((int64_t)1 << 31))
+        return RBA_E_UNSUPPORTED;
+    const Plan pl = make_plan(args);
+    if (num_splits == 0) {
+        const int cus = device_cus();
+        if (cus <= 0) return RBA_E_LAUNCH;
+        num_splits = heuristic_splits(args, pl, cus);
+    }
+    rba::AttnParams p = make_params(args, pl, num_splits);
+    p.kv32 = 0;
+    p.block_table = kv->block_table;
+    p.seq_lens = kv->seq_lens;
+    p.bt_stride = kv->bt_stride;
+    p.page_size = kv->page_size;
+    p.num_pages = kv->num_pages;
+    hipStream_t s = (hipStream_t)stream;
+    if (num_splits == 1) return rba::launch_attention(p, pl.var, s) == hipSuccess ? RBA_OK : RBA_E_LAUNCH;
+    const size_t need = workspace_bytes(args, num_splits);
+    if (workspace == nullptr || workspace_bytes_ < need || !aligned(workspace, 16)) return RBA_E_WORKSPACE;
     const size_t rows = (size_t)args->B * args->Sq * args->Hq;
     p.o_part = (float *)workspace;
     p.lse_part = p.o_part + (size_t)num_splits * rows * kHeadDim;

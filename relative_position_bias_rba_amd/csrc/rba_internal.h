@@ -25,6 +25,15 @@ struct AttnParams {
     int splits;          // key-range splits per block
     int r_vec;           // R rows allow 16-byte chunk loads
     int kv32;            // K and V of one (batch, kv head) span less than 2^31 bytes
+    // Paged K/V (block_table != null): k and v point to page pools, ks0/vs0
+    // are page strides, and sequence b has seq_lens[b] keys stored in pages
+    // block_table[b * bt_stride + i], page_size keys each (a multiple of the
+    // key tile).  Null for contiguous K/V.
+    const int *block_table;
+    const int *seq_lens;
+    int64_t bt_stride;
+    int page_size;
+    int num_pages;
 };
 
 // Kernel variants.  WIDE: two 32-column tiles per wave (prefill, bf16).

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for must in ("rba_relproj", "rba_attn_prefill", "rba_attn_decode", "rba_splitkv_combine",
+    for must in ("rba_relproj", "rba_attn_prefill", "rba_attn_decode", "rba_attn_paged", "rba_splitkv_combine",
                  "rba_num_splits", "rba_decode_workspace_bytes", "rba_status_string"):
         assert must in names
 
@@ -129,6 +129,57 @@ def test_decode_workspace_checks():
     assert lib.rba_splitkv_combine(None, None, 4, ctypes.byref(a), None) == RBA_E_INVALID
     assert lib.rba_splitkv_combine(ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(buf.data_ptr()), 0,
                                    ctypes.byref(a), None) == RBA_E_INVALID
+
+
+def _paged(B=2, Sq=3, ps=64, n_pages=10, Hq=8, Hkv=2, E=16, n_max=4):
+    q = torch.zeros(B, Sq, Hq, 128, dtype=torch.bfloat16)
+    kp = torch.zeros(n_pages, ps, Hkv, 128, dtype=torch.bfloat16)
+    vp = torch.zeros_like(kp)
+    R = torch.zeros(B, Sq, Hq, E, dtype=torch.bfloat16)
+    o = torch.zeros_like(q)
+    table = torch.zeros(B, n_max, dtype=torch.int32)
+    lens = torch.full((B,), ps * n_max, dtype=torch.int32)
+    a = make_args(q, kp, vp, R, o)
+    a.Skv = ps * n_max
+    kv = rba.make_paged(table, lens, ps, n_pages)
+    return a, kv, (q, kp, vp, R, o, table, lens)
+
+
+def _paged_call(a, kv, splits=1, ws=None, nbytes=0):
+    return lib.rba_attn_paged(ctypes.byref(a), None if kv is None else ctypes.byref(kv), splits, ws, nbytes, None)
+
+
+def test_paged_validation():
+    a, kv, keep = _paged()
+    assert _paged_call(a, None) == RBA_E_INVALID
+    for field, val in (("page_size", 0), ("page_size", 32), ("page_size", 96), ("num_pages", 0),
+                       ("bt_stride", 3), ("block_table", None), ("seq_lens", None)):
+        a, kv, keep = _paged()
+        setattr(kv, field, val)
+        assert _paged_call(a, kv) == RBA_E_INVALID, field
+    a, kv, keep = _paged()
+    kv.seq_lens = keep[6].data_ptr() + 2
+    assert _paged_call(a, kv) == RBA_E_INVALID
+    a, kv, keep = _paged()
+    a.Skv = 4 * 64 + 1               # needs a fifth table column
+    assert _paged_call(a, kv) == RBA_E_INVALID
+    a, kv, keep = _paged()
+    assert _paged_call(a, kv, splits=-1) == RBA_E_INVALID
+    assert _paged_call(a, kv, splits=4) == RBA_E_WORKSPACE
+    a, kv, keep = _paged()
+    a.d = 64
+    assert _paged_call(a, kv) == RBA_E_UNSUPPORTED
+    # a page whose K rows span 2^31 bytes cannot be addressed
+    a, kv, keep = _paged()
+    a.k_s[1] = 1 << 25
+    assert _paged_call(a, kv) == RBA_E_UNSUPPORTED
+
+
+def test_paged_empty_is_noop():
+    a, kv, keep = _paged(Sq=0)
+    kv.block_table = None
+    kv.seq_lens = None
+    assert _paged_call(a, kv, splits=3) == RBA_OK
 
 
 def test_relproj_validation():

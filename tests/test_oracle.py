@@ -15,8 +15,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (attention, attention_partial, attention_rows, brute_attention,
-                    log_scale_factor, lse_combine, relproj)
+from oracle import (attention, attention_paged, attention_partial, attention_rows, brute_attention,
+                    gather_pages, log_scale_factor, lse_combine, relproj)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
 
@@ -299,3 +299,71 @@ def test_lse_combine_all_empty_rows():
     lp = np.full((3, 2), -np.inf)
     o, l = lse_combine(op, lp)
     assert np.all(o == 0.0) and np.all(np.isneginf(l))
+
+
+# --------------------------------------------------------------------------- paged cache
+
+def _scatter_to_pages(dense_seqs, page_size, order, n_pages):
+    """Write each sequence's keys page by page into a pool, pages taken in
+    ``order``; returns pool [n_pages, page_size, H, d] (unused rows NaN) and
+    the table.  The inverse of reading a paged cache, written as stores."""
+    H, d = dense_seqs[0].shape[1:]
+    pool = np.full((n_pages, page_size, H, d), np.nan)
+    n_max = max(-(-len(x) // page_size) for x in dense_seqs)
+    table = -np.ones((len(dense_seqs), n_max), dtype=np.int64)
+    it = iter(order)
+    for b, x in enumerate(dense_seqs):
+        for i in range(-(-len(x) // page_size)):
+            pg = next(it)
+            table[b, i] = pg
+            chunk = x[i * page_size:(i + 1) * page_size]
+            pool[pg, :len(chunk)] = chunk
+    return pool, table
+
+
+@pytest.mark.parametrize("window,base", [(0, 0.0), (4, 0.0), (0, 100.0)])
+def test_paged_matches_brute_force_per_sequence(window, base):
+    lens, Sq, Hq, Hkv, d, E, ps = [11, 4, 8], 3, 4, 2, 8, 6, 4
+    ks = [_rand((L, Hkv, d), 10 + b) for b, L in enumerate(lens)]
+    vs = [_rand((L, Hkv, d), 20 + b) for b, L in enumerate(lens)]
+    q = _rand((len(lens), Sq, Hq, d), 30)
+    R = _rand((len(lens), Sq, Hq, E), 31)
+    order = [5, 0, 7, 2, 6, 3, 1, 4]          # 3 + 1 + 2 pages used, 2 spare
+    kp, table = _scatter_to_pages(ks, ps, order, 8)
+    vp, table2 = _scatter_to_pages(vs, ps, order, 8)
+    assert (table == table2).all()
+    o, lse = attention_paged(q, kp, vp, table, lens, R, window=window, log_scale_base=base)
+    assert np.isfinite(o).all()
+    for b, L in enumerate(lens):
+        ob, lb = brute_attention(q[b:b + 1], ks[b][None], vs[b][None], R[b:b + 1], window=window,
+                                 log_scale_base=base)
+        np.testing.assert_allclose(o[b], ob[0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[b], lb[0], rtol=1e-12, atol=1e-12)
+
+
+def test_paged_invariant_under_page_relabelling():
+    ps, Hkv, d, Sq, Hq = 4, 1, 8, 2, 2
+    pool_k = _rand((6, ps, Hkv, d), 40)
+    pool_v = _rand((6, ps, Hkv, d), 41)
+    table = np.array([[3, 1, 4], [0, 5, -1]])
+    lens = [10, 7]
+    q = _rand((2, Sq, Hq, d), 42)
+    o, lse = attention_paged(q, pool_k, pool_v, table, lens)
+    perm = np.array([2, 5, 0, 4, 1, 3])        # page i moves to slot perm[i]
+    pk2 = np.empty_like(pool_k)
+    pv2 = np.empty_like(pool_v)
+    pk2[perm] = pool_k
+    pv2[perm] = pool_v
+    t2 = np.where(table >= 0, perm[np.maximum(table, 0)], -1)
+    o2, lse2 = attention_paged(q, pk2, pv2, t2, lens)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def test_gather_pages_reads_rows_in_key_order():
+    # page p row i holds the value 100 p + i: key j of a sequence is then
+    # 100 table[j // ps] + j % ps
+    ps = 4
+    pool = (100 * np.arange(5)[:, None] + np.arange(ps)[None, :]).astype(float)[:, :, None, None]
+    got = gather_pages(pool, [3, 0, 4], 10)[:, 0, 0]
+    assert list(got) == [300, 301, 302, 303, 0, 1, 2, 3, 400, 401]

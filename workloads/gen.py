@@ -30,3 +30,43 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
     P = randn((w.Hq, w.r_dim, w.E), g, w.p_std)
     dt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
     return {n: t.to(dt) for n, t in (("q", q), ("k", k), ("v", v), ("r", r), ("P", P))}
+
+
+def make_paged_inputs(w: Workload, page_size: int, seq_lens=None, seed: int | None = None,
+                      spare_pages: int = 3) -> dict:
+    """CPU tensors for a paged KV cache with ``w``'s shapes.
+
+    q, r, P as in ``make_inputs``.  Sequence b holds seq_lens[b] keys (drawn
+    uniformly from [Sq, Skv] unless given); its pages are distinct pages of a
+    shared pool, assigned in a random order:
+      k_pool, v_pool : [num_pages, page_size, Hkv, d]
+      block_table    : int32 [B, ceil(Skv / page_size)]; entries past a
+                       sequence's last page are -1
+      seq_lens       : int32 [B]
+    The pool holds ``spare_pages`` pages that no sequence uses.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    q = randn((w.B, w.Sq, w.Hq, w.d), g, w.qk_std)
+    if seq_lens is None:
+        lens = torch.randint(w.Sq, w.Skv + 1, (w.B,), generator=g, dtype=torch.int64)
+    else:
+        lens = torch.as_tensor(seq_lens, dtype=torch.int64)
+    need = [(int(n) + page_size - 1) // page_size for n in lens]
+    n_pages = sum(need) + spare_pages
+    perm = torch.randperm(n_pages, generator=g)
+    n_max = (w.Skv + page_size - 1) // page_size
+    table = torch.full((w.B, n_max), -1, dtype=torch.int32)
+    at = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[at:at + n].to(torch.int32)
+        at += n
+    k_pool = randn((n_pages, page_size, w.Hkv, w.d), g, w.qk_std)
+    v_pool = randn((n_pages, page_size, w.Hkv, w.d), g, w.v_std)
+    r = randn((w.B, w.Sq, w.r_dim), g, w.r_std)
+    P = randn((w.Hq, w.r_dim, w.E), g, w.p_std)
+    dt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    out = {n: t.to(dt) for n, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("r", r), ("P", P))}
+    out["block_table"] = table
+    out["seq_lens"] = lens.to(torch.int32)
+    return out
