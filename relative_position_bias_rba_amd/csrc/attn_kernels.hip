@@ -128,6 +128,12 @@ __device__ __forceinline__ float max_across_halves(float x) {
     return fmaxf(a, b);
 }
 
+// A wave-uniform 32-bit read through the scalar data cache (a read-only
+// use of that cache: the kernel never writes the table it reads).
+__device__ __forceinline__ int load_scalar(const int *ptr) {
+    return *(const __attribute__((address_space(4))) int *)ptr;
+}
+
 // Buffer descriptor words for dma16_untracked (same layout as make_rsrc).
 __device__ __forceinline__ u32x4 make_rsrc_words(const void *base, int64_t bytes) {
     const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
@@ -324,9 +330,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     // Rows j0 .. of K or V; rows past the sequence (or the page) read zeros.
     auto kv_rsrc = [&](const T *g, int64_t pstride, int64_t stride, int j0) {
         if constexpr (PG) {
-            const int pg = j0 / p.page_size;
+            const int pg = __builtin_amdgcn_readfirstlane(j0 / p.page_size);   // wave-uniform
             const int off = j0 - pg * p.page_size;
-            const int page = min(max(p.block_table[(int64_t)b * p.bt_stride + pg], 0), p.num_pages - 1);
+            // through the scalar cache: a vector load would sit in the in-order
+            // vector-memory queue and make the tile's staging wait for it
+            const int page = min(max(load_scalar(p.block_table + (int64_t)b * p.bt_stride + pg), 0), p.num_pages - 1);
             const int rows = min(p.page_size - off, Skv - j0);
             return make_rsrc(g + (int64_t)page * pstride + (int64_t)off * stride,
                              ((int64_t)(rows - 1) * stride + D) * ES);
