@@ -265,7 +265,7 @@ def main():
                             max(args.steps, 10), torch)
     r2 = d["r"].reshape(-1, w.r_dim)
     ms_relproj = time_launches(c_launcher(rba, "rba_relproj", 1, 1, r2.shape[0], w.Hq, w.r_dim, w.E,
-                                          ctypes.c_void_p(r2.data_ptr()), r2.stride(0),
+                                          ctypes.c_void_p(r2.data_ptr()), r2.stride(0), 0,
                                           ctypes.c_void_p(d["P"].data_ptr()), ctypes.c_void_p(R.data_ptr()),
                                           rba._stream(dev)),
                                max(args.steps, 10), torch)

@@ -86,15 +86,20 @@ typedef struct rba_attn_args {
     int64_t q_s[3], k_s[3], v_s[3], o_s[3], R_s[3];
 } rba_attn_args;
 
-/* R = r . P per head  ([S-RPB], the relative-logit projection).
- *   r : [T, r_dim] (in_dt), row stride r_stride_t elements, channel contiguous
+/* R = r . P per head  ([S-RPB], the relative-logit projection):
+ *     R[t, h, e] = sum_c r[t, (h,) c] * P[h, c, e]
+ *   r : [T, r_dim] shared by all heads (r_stride_h = 0), or [T, Hq, r_dim]
+ *       one feature per head (r_stride_h >= r_dim); token stride r_stride_t
+ *       (>= r_dim, resp. >= Hq * r_stride_h) and head stride r_stride_h in
+ *       elements, channel contiguous, in_dt
  *   P : [Hq, r_dim, E] (in_dt), contiguous
  *   R : [T, Hq, E] (out_dt), contiguous
  * in_dt/out_dt may each be RBA_BF16 or RBA_FP32 (fp32 accumulation always;
  * bf16 output is rounded to nearest even).  1 <= r_dim <= 128, E >= 1.
  * T = 0 is a no-op.                                                          */
 rba_status rba_relproj(rba_dtype in_dt, rba_dtype out_dt, int64_t T, int Hq, int r_dim, int E,
-                       const void *r, int64_t r_stride_t, const void *P, void *R, void *stream);
+                       const void *r, int64_t r_stride_t, int64_t r_stride_h, const void *P, void *R,
+                       void *stream);
 
 /* Attention over all keys for every query row ([S-RPB], [V-ARCH]); one pass,
  * no workspace.  Any 1 <= Sq <= Skv is accepted (rows bottom-right aligned);

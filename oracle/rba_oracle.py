@@ -30,7 +30,8 @@ prose only; no listing, worked example or numbers exist for this path):
 Readings taken where the pages leave a step open (each is one line in the
 design notes):
   * r is one vector per token shared by all heads; P is one matrix per query
-    head, P[h] of shape [r_dim, E].
+    head, P[h] of shape [r_dim, E].  (relproj also takes one r per head,
+    the other reading, for callers whose r is per head.)
   * The bucket of distance p-j is p-j itself; R has exactly E entries and
     distances >= E get bias 0.
   * scale multiplies q.k only; the bias is added unscaled.
@@ -79,12 +80,21 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def relproj(r, P):
+def relproj(r, P, per_head=False):
     """R[..., h, e] = sum_c r[..., c] * P[h, c, e]   ([S-RPB]: P projects r to
-    per-head relative logits).  r: [..., r_dim]; P: [Hq, r_dim, E]."""
+    per-head relative logits).  r: [..., r_dim]; P: [Hq, r_dim, E].
+    per_head: r is [..., Hq, r_dim], one feature per head (the alternative
+    reading of r's shape), and R[..., h, e] = sum_c r[..., h, c] * P[h, c, e]."""
     r = _f64(r)
     P = _f64(P)
     Hq, r_dim, E = P.shape
+    if per_head:
+        lead = r.shape[:-2]
+        flat = r.reshape(-1, Hq, r_dim)
+        out = np.empty((flat.shape[0], Hq, E), dtype=np.float64)
+        for h in range(Hq):
+            out[:, h, :] = flat[:, h, :] @ P[h]
+        return out.reshape(*lead, Hq, E)
     flat = r.reshape(-1, r_dim)
     out = np.empty((flat.shape[0], Hq, E), dtype=np.float64)
     for h in range(Hq):

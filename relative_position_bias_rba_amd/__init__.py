@@ -72,7 +72,7 @@ def _load():
     lib = ctypes.CDLL(lib_path)
     P = ctypes.POINTER(_AttnArgs)
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    lib.rba_relproj.argtypes = [ci, ci, i64, ci, ci, ci, vp, i64, vp, vp, vp]
+    lib.rba_relproj.argtypes = [ci, ci, i64, ci, ci, ci, vp, i64, i64, vp, vp, vp]
     lib.rba_relproj.restype = ci
     lib.rba_attn_prefill.argtypes = [P, vp]
     lib.rba_attn_prefill.restype = ci
@@ -148,20 +148,34 @@ def _check_attn_inputs(q, k, v, R):
         raise TypeError("q, k, v and R must share one dtype")
 
 
-def relproj(r: torch.Tensor, P: torch.Tensor, out_dtype=None) -> torch.Tensor:
-    """R[..., h, e] = sum_c r[..., c] P[h, c, e] on the GPU (MFMA kernel)."""
+def relproj(r: torch.Tensor, P: torch.Tensor, out_dtype=None, per_head: bool = False) -> torch.Tensor:
+    """R[..., h, e] = sum_c r[..., c] P[h, c, e] on the GPU (MFMA kernel).
+
+    per_head=True: r is [..., Hq, r_dim], one feature per head, and
+    R[..., h, e] = sum_c r[..., h, c] P[h, c, e]."""
     if not (r.is_cuda and P.is_cuda):
         raise ValueError("tensors must live on the GPU")
     Hq, r_dim, E = P.shape
     if r.shape[-1] != r_dim:
         raise ValueError("r_dim mismatch")
     P = P.contiguous()
-    r2 = r.reshape(-1, r_dim)
-    if r2.stride(1) != 1:
-        r2 = r2.contiguous()
+    if per_head:
+        if r.dim() < 2 or r.shape[-2] != Hq:
+            raise ValueError("per-head r must be [..., Hq, r_dim]")
+        lead = r.shape[:-2]
+        r3 = r.reshape(-1, Hq, r_dim)
+        if r3.stride(2) != 1 or r3.stride(0) < Hq * r3.stride(1):
+            r3 = r3.contiguous()
+        rp, n, st, sh = r3, r3.shape[0], r3.stride(0), r3.stride(1)
+    else:
+        lead = r.shape[:-1]
+        r2 = r.reshape(-1, r_dim)
+        if r2.stride(1) != 1:
+            r2 = r2.contiguous()
+        rp, n, st, sh = r2, r2.shape[0], r2.stride(0), 0
     out_dtype = r.dtype if out_dtype is None else out_dtype
-    R = torch.empty(*r.shape[:-1], Hq, E, dtype=out_dtype, device=r.device)
-    code = _lib.rba_relproj(_dt(r), _dt(R), r2.shape[0], Hq, r_dim, E, _ptr(r2), r2.stride(0),
+    R = torch.empty(*lead, Hq, E, dtype=out_dtype, device=r.device)
+    code = _lib.rba_relproj(_dt(r), _dt(R), n, Hq, r_dim, E, _ptr(rp), st, sh,
                             _ptr(P), _ptr(R), _stream(r.device))
     _check("rba_relproj", code)
     return R

@@ -148,7 +148,7 @@ size_t workspace_bytes(const rba_attn_args *a, int splits) {
 extern "C" {
 
 rba_status rba_relproj(rba_dtype in_dt, rba_dtype out_dt, int64_t T, int Hq, int r_dim, int E, const void *r,
-                       int64_t r_stride_t, const void *P, void *R, void *stream) {
+                       int64_t r_stride_t, int64_t r_stride_h, const void *P, void *R, void *stream) {
     if ((in_dt != RBA_BF16 && in_dt != RBA_FP32) || (out_dt != RBA_BF16 && out_dt != RBA_FP32))
         return RBA_E_UNSUPPORTED;
     if (T < 0 || Hq < 1 || r_dim < 1 || E < 1) return RBA_E_INVALID;
@@ -156,9 +156,10 @@ rba_status rba_relproj(rba_dtype in_dt, rba_dtype out_dt, int64_t T, int Hq, int
     if (T == 0) return RBA_OK;
     if (r == nullptr || P == nullptr || R == nullptr) return RBA_E_INVALID;
     if (!aligned(r, 16) || !aligned(P, 16) || !aligned(R, 16)) return RBA_E_INVALID;
-    if (r_stride_t < r_dim) return RBA_E_INVALID;
+    if (r_stride_h != 0 && r_stride_h < r_dim) return RBA_E_INVALID;
+    if (r_stride_t < (r_stride_h == 0 ? (int64_t)r_dim : r_stride_h * Hq)) return RBA_E_INVALID;
     const hipError_t e = rba::launch_relproj(in_dt == RBA_BF16, out_dt == RBA_BF16, T, Hq, r_dim, E, r, r_stride_t,
-                                             P, R, (hipStream_t)stream);
+                                             r_stride_h, P, R, (hipStream_t)stream);
     return e == hipSuccess ? RBA_OK : RBA_E_LAUNCH;
 }
 

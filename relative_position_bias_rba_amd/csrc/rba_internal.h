@@ -49,6 +49,6 @@ hipError_t launch_combine(const float *o_part, const float *lse_part, int splits
                           hipStream_t stream);
 
 hipError_t launch_relproj(bool in_bf16, bool out_bf16, int64_t T, int Hq, int r_dim, int E, const void *r,
-                          int64_t r_stride, const void *P, void *R, hipStream_t stream);
+                          int64_t r_stride, int64_t r_stride_h, const void *P, void *R, hipStream_t stream);
 
 }  // namespace rba

@@ -45,7 +45,8 @@ __device__ __forceinline__ int lds_row(int j) { return j ^ (((j >> 4) & 1) * 12)
 // sizes the register file use, and with it how many waves a CU keeps in flight
 // to stream the output.
 template <typename TI, typename TO, int NK>
-__global__ __launch_bounds__(NT) void relproj_kernel(const TI *__restrict__ r, int64_t rs, const TI *__restrict__ P,
+__global__ __launch_bounds__(NT) void relproj_kernel(const TI *__restrict__ r, int64_t rs, int64_t rsh,
+                                                     const TI *__restrict__ P,
                                                      TO *__restrict__ R, int64_t T, int Hq, int r_dim, int E, int EC,
                                                      int NTB) {
     constexpr bool BF = sizeof(TI) == 2;
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(NT) void relproj_kernel(const TI *__restrict__ r, i
     const int64_t xb = blockIdx.x / ((unsigned)nz * (unsigned)Hq);
     const int KP = (r_dim + 15) & ~15;     // channels padded to a 16-multiple
     const int PS = KP + PAD;               // LDS row stride
-    const bool r_vec = (r_dim % 8 == 0) && (rs % 8 == 0);
+    const bool r_vec = (r_dim % 8 == 0) && (rs % 8 == 0) && (rsh % 8 == 0);
     const bool e_vec = (E % (16 / (int)sizeof(TO))) == 0;
     const int nks = BF ? KP / 16 : KP / 2;
     const int arow_key = mfma_row_key(lc);
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(NT) void relproj_kernel(const TI *__restrict__ r, i
     for (int c = 0; c < TT; ++c) {
         const int64_t t = tbase + 32 * c + lc;
         const bool ok = t < T;
-        const TI *rp = r + (ok ? t : 0) * rs;
+        const TI *rp = r + (ok ? t : 0) * rs + (int64_t)h * rsh;   // rsh = 0: r shared by all heads
         if constexpr (BF) {
 #pragma unroll
             for (int k = 0; k < NK; ++k) {
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(NT) void relproj_kernel(const TI *__restrict__ r, i
 }  // namespace
 
 hipError_t launch_relproj(bool in_bf16, bool out_bf16, int64_t T, int Hq, int r_dim, int E, const void *r,
-                          int64_t r_stride, const void *P, void *R, hipStream_t stream) {
+                          int64_t r_stride, int64_t r_stride_h, const void *P, void *R, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     // distances per workgroup: the largest of 256 / 128 / 64 whose P^T chunk fits 64 KiB of LDS
     const int es = in_bf16 ? 2 : 4;
@@ -261,23 +262,23 @@ hipError_t launch_relproj(bool in_bf16, bool out_bf16, int64_t T, int Hq, int r_
     if (in_bf16 && out_bf16) {
         if (k4)
             hipLaunchKernelGGL((relproj_kernel<__bf16, __bf16, 4>), grid, block, lds, stream, (const __bf16 *)r,
-                               r_stride, (const __bf16 *)P, (__bf16 *)R, T, Hq, r_dim, E, EC, NTB);
+                               r_stride, r_stride_h, (const __bf16 *)P, (__bf16 *)R, T, Hq, r_dim, E, EC, NTB);
         else
             hipLaunchKernelGGL((relproj_kernel<__bf16, __bf16, 8>), grid, block, lds, stream, (const __bf16 *)r,
-                               r_stride, (const __bf16 *)P, (__bf16 *)R, T, Hq, r_dim, E, EC, NTB);
+                               r_stride, r_stride_h, (const __bf16 *)P, (__bf16 *)R, T, Hq, r_dim, E, EC, NTB);
     } else if (in_bf16) {
         if (k4)
             hipLaunchKernelGGL((relproj_kernel<__bf16, float, 4>), grid, block, lds, stream, (const __bf16 *)r,
-                               r_stride, (const __bf16 *)P, (float *)R, T, Hq, r_dim, E, EC, NTB);
+                               r_stride, r_stride_h, (const __bf16 *)P, (float *)R, T, Hq, r_dim, E, EC, NTB);
         else
             hipLaunchKernelGGL((relproj_kernel<__bf16, float, 8>), grid, block, lds, stream, (const __bf16 *)r,
-                               r_stride, (const __bf16 *)P, (float *)R, T, Hq, r_dim, E, EC, NTB);
+                               r_stride, r_stride_h, (const __bf16 *)P, (float *)R, T, Hq, r_dim, E, EC, NTB);
     } else if (out_bf16) {
         hipLaunchKernelGGL((relproj_kernel<float, __bf16, 8>), grid, block, lds, stream, (const float *)r, r_stride,
-                           (const float *)P, (__bf16 *)R, T, Hq, r_dim, E, EC, NTB);
+                           r_stride_h, (const float *)P, (__bf16 *)R, T, Hq, r_dim, E, EC, NTB);
     } else {
         hipLaunchKernelGGL((relproj_kernel<float, float, 8>), grid, block, lds, stream, (const float *)r, r_stride,
-                           (const float *)P, (float *)R, T, Hq, r_dim, E, EC, NTB);
+                           r_stride_h, (const float *)P, (float *)R, T, Hq, r_dim, E, EC, NTB);
     }
     return hipGetLastError();
 }

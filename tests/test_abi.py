@@ -111,7 +111,7 @@ def test_empty_inputs_are_noops():
     assert _prefill(a) == RBA_OK
     r = torch.zeros(0, 64)
     P = torch.zeros(4, 64, 16)
-    assert lib.rba_relproj(0, 0, 0, 4, 64, 16, None, 64, None, None, None) == RBA_OK
+    assert lib.rba_relproj(0, 0, 0, 4, 64, 16, None, 64, 0, None, None, None) == RBA_OK
 
 
 def test_decode_workspace_checks():
@@ -187,14 +187,18 @@ def test_relproj_validation():
     P = torch.zeros(4, 64, 16, dtype=torch.bfloat16)
     R = torch.zeros(8, 4, 16, dtype=torch.bfloat16)
     pr, pP, pR = (ctypes.c_void_p(t.data_ptr()) for t in (r, P, R))
-    assert lib.rba_relproj(1, 1, 8, 4, 200, 16, pr, 200, pP, pR, None) == RBA_E_UNSUPPORTED
-    assert lib.rba_relproj(1, 1, 8, 4, 0, 16, pr, 64, pP, pR, None) == RBA_E_INVALID
-    assert lib.rba_relproj(1, 1, 8, 4, 64, 0, pr, 64, pP, pR, None) == RBA_E_INVALID
-    assert lib.rba_relproj(1, 1, -1, 4, 64, 16, pr, 64, pP, pR, None) == RBA_E_INVALID
-    assert lib.rba_relproj(1, 1, 8, 4, 64, 16, None, 64, pP, pR, None) == RBA_E_INVALID
-    assert lib.rba_relproj(1, 1, 8, 4, 64, 16, pr, 32, pP, pR, None) == RBA_E_INVALID
-    assert lib.rba_relproj(1, 1, 8, 4, 64, 16, ctypes.c_void_p(r.data_ptr() + 2), 64, pP, pR, None) == RBA_E_INVALID
-    assert lib.rba_relproj(3, 1, 8, 4, 64, 16, pr, 64, pP, pR, None) == RBA_E_UNSUPPORTED
+    assert lib.rba_relproj(1, 1, 8, 4, 200, 16, pr, 200, 0, pP, pR, None) == RBA_E_UNSUPPORTED
+    assert lib.rba_relproj(1, 1, 8, 4, 0, 16, pr, 64, 0, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(1, 1, 8, 4, 64, 0, pr, 64, 0, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(1, 1, -1, 4, 64, 16, pr, 64, 0, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(1, 1, 8, 4, 64, 16, None, 64, 0, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(1, 1, 8, 4, 64, 16, pr, 32, 0, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(1, 1, 8, 4, 64, 16, ctypes.c_void_p(r.data_ptr() + 2), 64, 0, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(3, 1, 8, 4, 64, 16, pr, 64, 0, pP, pR, None) == RBA_E_UNSUPPORTED
+    # per-head r: head stride below r_dim, or token stride below Hq head strides
+    assert lib.rba_relproj(1, 1, 8, 4, 64, 16, pr, 256, 32, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(1, 1, 8, 4, 64, 16, pr, 200, 64, pP, pR, None) == RBA_E_INVALID
+    assert lib.rba_relproj(1, 1, 8, 4, 64, 16, pr, 256, -64, pP, pR, None) == RBA_E_INVALID
 
 
 # --------------------------------------------------------------------------- split heuristic (host logic)

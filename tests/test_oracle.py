@@ -276,6 +276,26 @@ def test_relproj_small_brute_force():
                 assert abs(R[0, t, h, e] - s) <= 1e-14
 
 
+def test_relproj_per_head_brute_force_and_shared_case():
+    Hq, r_dim, E = 3, 4, 5
+    rh = _rand((2, 3, Hq, r_dim), 5)
+    P = _rand((Hq, r_dim, E), 6)
+    R = relproj(rh, P, per_head=True)
+    assert R.shape == (2, 3, Hq, E)
+    for b in range(2):
+        for t in range(3):
+            for h in range(Hq):
+                for e in range(E):
+                    s = 0.0
+                    for c in range(r_dim):
+                        s += rh[b, t, h, c] * P[h, c, e]
+                    assert abs(R[b, t, h, e] - s) <= 1e-14
+    # every head holding the same feature reduces to the shared form
+    r = _rand((2, 3, r_dim), 7)
+    same = np.repeat(r[:, :, None, :], Hq, axis=2)
+    assert np.array_equal(relproj(same, P, per_head=True), relproj(r, P))
+
+
 # --------------------------------------------------------------------------- combine
 
 @pytest.mark.parametrize("bounds", [[0, 13], [0, 5, 13], [0, 1, 2, 7, 13], [0, 13, 13, 13], [0, 4, 4, 9, 13]])

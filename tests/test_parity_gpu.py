@@ -83,6 +83,27 @@ def test_relproj_parity(T, Hq, r_dim, E, dt, odt):
     check(f"relproj {T}x{Hq}x{r_dim}x{E}", R, want, fp32)
 
 
+@pytest.mark.parametrize("T,Hq,r_dim,E,dt,sliced", [
+    (200, 4, 64, 96, torch.bfloat16, False),
+    (77, 3, 40, 100, torch.bfloat16, True),     # rows not 16-byte aligned: element loads
+    (130, 2, 32, 64, torch.float32, False),
+])
+def test_relproj_per_head_parity(T, Hq, r_dim, E, dt, sliced):
+    say(f"relproj per-head T={T} Hq={Hq} r_dim={r_dim} E={E} {dt} sliced={sliced}")
+    g = torch.Generator().manual_seed(T + 13 * E)
+    full = torch.randn(T, Hq, r_dim + (3 if sliced else 0), generator=g).to(dt)
+    r = full[..., :r_dim]                       # head stride r_dim (+3 when sliced)
+    P = (torch.randn(Hq, r_dim, E, generator=g) * 0.02).to(dt)
+    R = rba().relproj(full.to(DEV)[..., :r_dim], P.to(DEV), per_head=True)
+    torch.cuda.synchronize()
+    want = oracle.relproj(r, P, per_head=True)
+    if dt == torch.float32:
+        check("relproj per-head", R, want, True)
+    else:
+        g_ = R.double().cpu().numpy()
+        assert np.all(np.abs(g_ - want) <= 2.0 ** -8 * np.abs(want) + 1e-6)
+
+
 # --------------------------------------------------------------------------- prefill, small shapes, every element
 
 def run_path(inp, w, *, decode=False, splits=0, return_lse=True):
