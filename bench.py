@@ -7,7 +7,9 @@ prefill, with all inputs resident in HBM.  `value` is attention TFLOP/s
 (4*d*Hq flops per visible query/key pair) over the whole step.  The same JSON
 line carries the kernel-level roofline of the dominant kernel (attention,
 timed with HIP events on the stream it runs on), the split-KV decode
-workloads' KV GB/s, and the fp64 CPU oracle timed on a bounded sample.
+workloads' KV GB/s, the streaming-read bandwidth and MFMA rate the device
+attains (each rate is also given as a fraction of those), and the fp64 CPU
+oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
 """
@@ -208,6 +210,28 @@ def paged_decode_leg(rba, torch, name, page_size, reps, len_lo, seed=77):
     return res
 
 
+def attainable(rba, torch):
+    """Streaming-read bandwidth and bf16 MFMA rate this device attains (the library's
+    measurement aids, timed like the kernels)."""
+    dev = torch.device("cuda")
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    st = rba._stream(dev)
+    rd = c_launcher(rba, "rba_calib_read", ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), st)
+    ms_rd = time_launches(rd, 10, torch)
+    flops = ctypes.c_double(0.0)
+    iters = 250
+    mm = c_launcher(rba, "rba_calib_mfma", iters, ctypes.c_void_p(sink.data_ptr()), ctypes.byref(flops), st)
+    ms_mm = time_launches(mm, 5, torch)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBps": round(nbytes / (ms_rd * 1e-3) / 1e9, 1),
+            "mfma_bf16_TFLOPs": round(flops.value / (ms_mm * 1e-3) / 1e12, 1),
+            "how": "rba_calib_read over 2 GiB (16-byte loads, 2 workgroups per CU) and rba_calib_mfma "
+                   "(back-to-back bf16 32x32x16 MFMA, 32 waves per CU), HIP events, after a clock warm-up"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,6 +335,13 @@ def main():
         for name in ("c4_decode_swa", "c4_decode_full", "c5_long_decode"):
             out["decode"][name] = decode_leg(rba, torch, name, 20)
         out["decode"]["c4_decode_full_paged64"] = paged_decode_leg(rba, torch, "c4_decode_full", 64, 20, 8192)
+    att = attainable(rba, torch)
+    out["attainable"] = att
+    out["roofline"]["frac_attainable"] = round(out["roofline"]["achieved"] / att["mfma_bf16_TFLOPs"], 4)
+    for leg in out.get("decode", {}).values():
+        leg["frac_attainable"] = round(leg["kv_GBps"] / att["hbm_read_GBps"], 4)
+    out["device"] = {"name": torch.cuda.get_device_name(0), "hip": torch.version.hip,
+                     "compute_units": torch.cuda.get_device_properties(0).multi_processor_count}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(w, d_cpu, args.cpu_budget)

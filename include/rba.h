@@ -168,6 +168,20 @@ rba_status rba_attn_paged(const rba_attn_args *args, const rba_paged_kv *kv, int
 rba_status rba_splitkv_combine(const float *o_part, const float *lse_part, int num_splits,
                                const rba_attn_args *args, void *stream);
 
+/* Measurement aids (not part of the attention path).  They report what this
+ * device attains, so that the kernels' rates can be read against it as well
+ * as against the published peaks.
+ *   rba_calib_read : read `bytes` (a multiple of 16384) of device memory at
+ *                    `buf` once with 16-byte loads from 2 workgroups per CU;
+ *                    `sink` is 4 bytes of device memory that is (almost
+ *                    surely) left unwritten.  Time it with events.
+ *   rba_calib_mfma : 8 workgroups per CU of 4 waves each run `iters` x 4
+ *                    back-to-back bf16 32x32x16 matrix instructions; *flops
+ *                    (host, may be NULL) receives the flop count of the
+ *                    launch.  Same sink rule.                                */
+rba_status rba_calib_read(const void *buf, size_t bytes, void *sink, void *stream);
+rba_status rba_calib_mfma(int iters, void *sink, double *flops, void *stream);
+
 /* Static description of a status code. */
 const char *rba_status_string(rba_status status);
 

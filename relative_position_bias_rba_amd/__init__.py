@@ -88,6 +88,10 @@ def _load():
     lib.rba_splitkv_combine.restype = ci
     lib.rba_status_string.argtypes = [ci]
     lib.rba_status_string.restype = ctypes.c_char_p
+    lib.rba_calib_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+    lib.rba_calib_read.restype = ci
+    lib.rba_calib_mfma.argtypes = [ci, vp, ctypes.POINTER(ctypes.c_double), vp]
+    lib.rba_calib_mfma.restype = ci
     lib.rba_version.argtypes = []
     lib.rba_version.restype = ci
     return lib

@@ -16,6 +16,7 @@ constexpr int kHeadDim = 128;
 constexpr int kMaxSplits = 1024;
 constexpr int kMinTilesPerSplit = 4;
 constexpr int kPageQuantum = 64;   // paged K/V: a page holds whole 64-key tiles
+constexpr size_t kCalibReadQuantum = 16384;   // the read probe covers 1024 16-byte chunks per step
 
 int elem_size(rba_dtype dt) { return dt == RBA_BF16 ? 2 : 4; }
 
@@ -266,6 +267,26 @@ rba_status rba_splitkv_combine(const float *o_part, const float *lse_part, int n
         rba::launch_combine(o_part, lse_part, num_splits, args->B, args->Sq, args->Hq, args->o, args->dt == RBA_BF16,
                             args->o_s[0], args->o_s[1], args->o_s[2], args->lse, (hipStream_t)stream);
     return e == hipSuccess ? RBA_OK : RBA_E_LAUNCH;
+}
+
+rba_status rba_calib_read(const void *buf, size_t bytes, void *sink, void *stream) {
+    if (bytes == 0) return RBA_OK;
+    if (buf == nullptr || sink == nullptr || !aligned(buf, 16) || !aligned(sink, 4)) return RBA_E_INVALID;
+    if (bytes % kCalibReadQuantum != 0 || bytes > ((size_t)1 << 40)) return RBA_E_INVALID;
+    const int cus = device_cus();
+    if (cus <= 0) return RBA_E_LAUNCH;
+    return rba::launch_calib_read(buf, (int64_t)bytes, sink, 2 * cus, (hipStream_t)stream) == hipSuccess
+               ? RBA_OK
+               : RBA_E_LAUNCH;
+}
+
+rba_status rba_calib_mfma(int iters, void *sink, double *flops, void *stream) {
+    if (iters < 1 || sink == nullptr || !aligned(sink, 4)) return RBA_E_INVALID;
+    const int cus = device_cus();
+    if (cus <= 0) return RBA_E_LAUNCH;
+    const int blocks = 8 * cus;   // 32 waves per CU: eight per SIMD
+    if (flops != nullptr) *flops = (double)blocks * 4 /*waves*/ * iters * 4 /*MFMAs*/ * (2.0 * 32 * 32 * 16);
+    return rba::launch_calib_mfma(iters, blocks, sink, (hipStream_t)stream) == hipSuccess ? RBA_OK : RBA_E_LAUNCH;
 }
 
 const char *rba_status_string(rba_status status) {

@@ -51,4 +51,8 @@ hipError_t launch_combine(const float *o_part, const float *lse_part, int splits
 hipError_t launch_relproj(bool in_bf16, bool out_bf16, int64_t T, int Hq, int r_dim, int E, const void *r,
                           int64_t r_stride, int64_t r_stride_h, const void *P, void *R, hipStream_t stream);
 
+hipError_t launch_calib_read(const void *buf, int64_t bytes, void *sink, int blocks, hipStream_t stream);
+
+hipError_t launch_calib_mfma(int iters, int blocks, void *sink, hipStream_t stream);
+
 }  // namespace rba

@@ -182,6 +182,19 @@ def test_paged_empty_is_noop():
     assert _paged_call(a, kv, splits=3) == RBA_OK
 
 
+def test_calib_validation():
+    buf = torch.zeros(16384, dtype=torch.uint8)
+    sink = torch.zeros(4, dtype=torch.float32)
+    pb, ps = ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(sink.data_ptr())
+    assert lib.rba_calib_read(pb, 0, ps, None) == RBA_OK
+    assert lib.rba_calib_read(pb, 1000, ps, None) == RBA_E_INVALID
+    assert lib.rba_calib_read(None, 16384, ps, None) == RBA_E_INVALID
+    assert lib.rba_calib_read(pb, 16384, None, None) == RBA_E_INVALID
+    assert lib.rba_calib_read(ctypes.c_void_p(buf.data_ptr() + 4), 16384, ps, None) == RBA_E_INVALID
+    assert lib.rba_calib_mfma(0, ps, None, None) == RBA_E_INVALID
+    assert lib.rba_calib_mfma(10, None, None, None) == RBA_E_INVALID
+
+
 def test_relproj_validation():
     r = torch.zeros(8, 64, dtype=torch.bfloat16)
     P = torch.zeros(4, 64, 16, dtype=torch.bfloat16)

@@ -104,6 +104,23 @@ def test_relproj_per_head_parity(T, Hq, r_dim, E, dt, sliced):
         assert np.all(np.abs(g_ - want) <= 2.0 ** -8 * np.abs(want) + 1e-6)
 
 
+def test_calibration_kernels_run():
+    """The measurement aids launch, report their flop count and leave the sink alone."""
+    import ctypes
+    m = rba()
+    buf = torch.ones(1 << 24, dtype=torch.uint8, device=DEV)
+    sink = torch.zeros(4, dtype=torch.float32, device=DEV)
+    st = m._stream(torch.device(DEV))
+    assert m._lib.rba_calib_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), ctypes.c_void_p(sink.data_ptr()),
+                                 st) == 0
+    flops = ctypes.c_double(0.0)
+    assert m._lib.rba_calib_mfma(3, ctypes.c_void_p(sink.data_ptr()), ctypes.byref(flops), st) == 0
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert flops.value == 8 * cus * 4 * 3 * 4 * 2 * 32 * 32 * 16
+    assert torch.count_nonzero(sink).item() == 0
+
+
 # --------------------------------------------------------------------------- prefill, small shapes, every element
 
 def run_path(inp, w, *, decode=False, splits=0, return_lse=True):
