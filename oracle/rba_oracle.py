@@ -26,6 +26,13 @@ prose only; no listing, worked example or numbers exist for this path):
   [V-KV]   same page, section "vLLM テクニカル最適化": the serving engine
            keeps the caches of all layers in one unified KV cache manager and
            re-runs the multi-token-prediction heads over accepted tokens.
+  [S-FA4]  "SGLang と Miles が Inkling を初日からサポート", section "Relative
+           Attention と FA4 経路": the attention kernel runs in an MXFP8
+           configuration together with the sheared bias.  [V-FP8] "vLLM TML
+           Inkling サポート", section on future work: FP8 for global attention
+           to relieve compute and KV-cache limits.  MXFP8 itself is the OCP
+           Microscaling Formats (MX) v1.0 specification: blocks of 32 elements
+           share a power-of-two scale (E8M0), elements are FP8 E4M3.
 
 Readings taken where the pages leave a step open (each is one line in the
 design notes):
@@ -40,6 +47,12 @@ design notes):
   * Window W > 0: key j visible iff 0 <= p-j < W.  W = 0: full causal.
   * Query row t sits at position p = Skv - Sq + t.
   * GQA: query head h reads kv head h // (Hq/Hkv).
+  * MXFP8 ([S-FA4], OCP MX v1.0): a block's shared exponent is
+    floor(log2(amax)) - 8 (8 = exponent of E4M3's largest normal, 448),
+    clamped to [-127, 127], and -127 for an all-zero block; each element is
+    x / 2^e rounded to the nearest E4M3 value, ties to even, saturated to
+    +-448.  K and V are blocked along the head dimension (32 entries), and
+    attention with an MXFP8 cache is the attention over the decoded values.
   * Paged cache ([V-KV]): sequence b has its own length L_b; its key j is row
     j % page_size of page block_table[b][j // page_size] of a shared pool;
     its Sq query rows are its last Sq positions, L_b - Sq + t.
@@ -69,6 +82,9 @@ __all__ = [
     "brute_attention",
     "gather_pages",
     "attention_paged",
+    "e4m3_value",
+    "mxfp8_quantize",
+    "mxfp8_dequantize",
 ]
 
 
@@ -345,3 +361,74 @@ def attention_paged(q, k_pool, v_pool, block_table, seq_lens, R=None, *, window=
         o[b] = ob[0]
         lse[b] = lb[0]
     return o, lse
+
+
+# --------------------------------------------------------------------------- MXFP8 (OCP MX v1.0, E4M3 elements)
+
+E4M3_MAX = 448.0          # largest finite E4M3 value, 1.75 * 2^8
+E4M3_EMAX = 8             # its exponent
+MX_BLOCK = 32             # elements per shared scale
+
+
+def e4m3_value(code):
+    """Value of an OCP E4M3 bit pattern (sign, 4-bit exponent with bias 7,
+    3-bit mantissa; exponent field 0 is subnormal, S.1111.111 is NaN, no
+    infinities).  Works elementwise on integer arrays."""
+    code = np.asarray(code, dtype=np.int64)
+    sign = np.where(code & 0x80, -1.0, 1.0)
+    ef = (code >> 3) & 0xF
+    m = (code & 0x7).astype(np.float64)
+    val = np.where(ef == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, ef - 7))
+    val = np.where((ef == 15) & ((code & 7) == 7), np.nan, val)
+    return sign * val
+
+
+def _e4m3_encode(v):
+    """E4M3 code of each fp64 value v: nearest representable value, ties to
+    the even mantissa, magnitudes saturated to 448; -0 keeps its sign."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    # quantum: 2^(floor(log2 a) - 3) for normal magnitudes, 2^-9 below 2^-6
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))          # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, -6)
+    quantum = np.ldexp(1.0, e - 3)
+    q = np.round(a / quantum) * quantum                  # numpy rounds half to even
+    q = np.minimum(q, E4M3_MAX)
+    # bit pattern of q
+    _, qx = np.frexp(np.where(q > 0, q, 1.0))
+    qe = qx - 1
+    normal = q >= 2.0 ** -6
+    field = np.where(normal, qe + 7, 0)
+    mant = np.where(normal, q / np.ldexp(1.0, qe) * 8.0 - 8.0, q / 2.0 ** -9)
+    code = (field.astype(np.int64) << 3) | np.rint(mant).astype(np.int64)
+    code = np.where(q == 0, 0, code)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def mxfp8_quantize(x):
+    """MXFP8 encoding of x [..., n] (n a multiple of 32) along its last axis.
+
+    Returns (codes uint8 [..., n], scales uint8 [..., n/32]) where scales
+    hold the E8M0 codes e + 127 of the shared exponents."""
+    x = _f64(x)
+    n = x.shape[-1]
+    if n % MX_BLOCK:
+        raise ValueError("last axis must be a multiple of 32")
+    blocks = x.reshape(*x.shape[:-1], n // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))     # floor(log2 amax) = ex - 1
+    e = np.where(amax > 0, ex - 1 - E4M3_EMAX, -127)
+    e = np.clip(e, -127, 127)
+    scaled = blocks / np.ldexp(1.0, e)[..., None]
+    codes = _e4m3_encode(scaled).reshape(x.shape)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def mxfp8_dequantize(codes, scales):
+    """Decoded values (fp64) of MXFP8 codes [..., n] with scales [..., n/32]."""
+    codes = np.asarray(codes)
+    scales = np.asarray(scales).astype(np.int64)
+    n = codes.shape[-1]
+    vals = e4m3_value(codes).reshape(*codes.shape[:-1], n // MX_BLOCK, MX_BLOCK)
+    s = np.where(scales == 255, np.nan, np.ldexp(1.0, scales - 127))
+    return (vals * s[..., None]).reshape(codes.shape)

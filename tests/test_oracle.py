@@ -16,7 +16,9 @@ import pytest
 import torch
 
 from oracle import (attention, attention_paged, attention_partial, attention_rows, brute_attention,
-                    gather_pages, log_scale_factor, lse_combine, relproj)
+                    e4m3_value, gather_pages, log_scale_factor, lse_combine, mxfp8_dequantize, mxfp8_quantize,
+                    relproj)
+from oracle.rba_oracle import _e4m3_encode
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
 
@@ -387,3 +389,104 @@ def test_gather_pages_reads_rows_in_key_order():
     pool = (100 * np.arange(5)[:, None] + np.arange(ps)[None, :]).astype(float)[:, :, None, None]
     got = gather_pages(pool, [3, 0, 4], 10)[:, 0, 0]
     assert list(got) == [300, 301, 302, 303, 0, 1, 2, 3, 400, 401]
+
+
+# --------------------------------------------------------------------------- MXFP8 (OCP MX v1.0)
+
+def test_e4m3_table_closed_forms():
+    v = e4m3_value(np.arange(256))
+    assert v[0x00] == 0.0 and v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9
+    assert v[0x08] == 2.0 ** -6 and v[0x38] == 1.0 and v[0x39] == 1.125 and v[0x7E] == 448.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.sum(np.isnan(v)) == 2
+    assert v[0x80] == 0.0 and np.signbit(v[0x80]) and v[0xB8] == -1.0 and v[0xFE] == -448.0
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)                      # 127 increasing non-negative values
+    assert np.array_equal(v[0x80:0xFF], -pos)
+
+
+def _nearest_code(x):
+    """Brute force: the finite E4M3 code nearest to x (x clamped to +-448),
+    ties to the even code (even mantissa), zero keeping x's sign."""
+    tab = e4m3_value(np.arange(256))
+    xc = min(max(x, -448.0), 448.0)
+    best, bd = None, None
+    for c in range(256):
+        v = tab[c]
+        if np.isnan(v) or (v == 0 and bool(c & 0x80) != bool(np.signbit(xc))):
+            continue
+        d = abs(v - xc)
+        if bd is None or d < bd or (d == bd and c % 2 == 0):
+            best, bd = c, d
+    return best
+
+
+def test_e4m3_encode_matches_brute_force():
+    tab = e4m3_value(np.arange(256))
+    fin = tab[~np.isnan(tab)]
+    pos = np.sort(fin[fin > 0])
+    mids = (pos[:-1] + pos[1:]) / 2
+    rng = np.random.default_rng(5)
+    xs = np.concatenate([fin, mids, -mids, np.nextafter(mids, 1e9), np.nextafter(mids, -1e9),
+                         rng.standard_normal(300) * 50, rng.standard_normal(100) * 1e-2,
+                         [449.0, 463.9, 464.0, 464.1, 500.0, 1e6, -1e6, 0.0, -0.0, 2.0 ** -10, -(2.0 ** -10),
+                          3 * 2.0 ** -11, 1e-30]])
+    got = _e4m3_encode(xs)
+    for x, g in zip(xs, got):
+        assert int(g) == _nearest_code(float(x)), (x, g)
+
+
+def test_mxfp8_scale_rule_closed_forms():
+    def scale_of(block):
+        _, s = mxfp8_quantize(np.asarray(block, dtype=np.float64)[None, :])
+        return int(s[0, 0])
+    ones = np.ones(32)
+    assert scale_of(ones) == 127 - 8                      # amax 1 = 2^0 -> e = -8
+    assert scale_of(ones * 1.999) == 127 - 8
+    assert scale_of(ones * 2.0) == 127 - 7
+    assert scale_of(ones * 0.75) == 127 - 9               # floor(log2 0.75) = -1
+    assert scale_of(np.zeros(32)) == 0                    # all-zero block
+    assert scale_of(ones * 2.0 ** -140) == 0              # clamped at e = -127
+    assert scale_of(ones * 2.0 ** 200) == 254             # clamped at e = 127
+    b = np.zeros(32)
+    b[7] = -3.0                                           # the sign does not matter
+    assert scale_of(b) == 127 + 1 - 8
+
+
+def test_mxfp8_roundtrip_and_saturation():
+    # values on the grid of a common scale survive exactly
+    e = -5
+    tab = e4m3_value(np.arange(256))
+    fin = tab[~np.isnan(tab)]
+    rng = np.random.default_rng(9)
+    block = rng.choice(fin[np.abs(fin) <= 448], 32) * 2.0 ** e
+    block[0] = 288.0 * 2.0 ** e                           # amax in [256, 512) * 2^e -> scale 2^e; 288 is on the grid
+    c, s = mxfp8_quantize(block[None, :])
+    assert int(s[0, 0]) == e + 127
+    assert np.array_equal(mxfp8_dequantize(c, s)[0], block)
+    # amax in (464, 512) * 2^e saturates to 448 * 2^e
+    sat = np.full(32, 0.5)
+    sat[3] = 1.9                                          # 1.9 / 2^-8 = 486.4 > 448
+    c, s = mxfp8_quantize(sat[None, :])
+    d = mxfp8_dequantize(c, s)[0]
+    assert d[3] == 448.0 * 2.0 ** -8 and d[0] == 0.5
+
+
+def test_mxfp8_error_bound_and_brute_force():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((6, 128)) * np.array([1e-3, 0.1, 1, 10, 1e3, 1e5])[:, None]
+    x[2, 32:64] = 0.0
+    c, s = mxfp8_quantize(x)
+    d = mxfp8_dequantize(c, s)
+    for r in range(6):
+        for k in range(4):
+            blk = x[r, 32 * k:32 * k + 32]
+            e = int(s[r, k]) - 127
+            for i in range(32):
+                # brute force per element, scale taken from the rule
+                want = e4m3_value(_nearest_code(blk[i] / 2.0 ** e)) * 2.0 ** e
+                assert d[r, 32 * k + i] == want
+                # half a quantum of the element's binade (3 mantissa bits), or of the subnormal step
+                v = abs(blk[i]) / 2.0 ** e
+                if v <= 448:
+                    q = 2.0 ** (max(np.floor(np.log2(v)) if v > 0 else -6, -6) - 3)
+                    assert abs(d[r, 32 * k + i] - blk[i]) <= 0.5 * q * 2.0 ** e * (1 + 1e-12)
