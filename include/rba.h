@@ -16,6 +16,13 @@
  *            size 128; the relative term is added before softmax.
  *   [V-OPT]  same page, section "低レイテンシコレクティブとカーネル": the
  *            split-KV factor (num_splits) is chosen per batch size and KV length.
+ *   [S-FA4]  "SGLang と Miles が Inkling を初日からサポート", section "Relative
+ *            Attention と FA4 経路": the attention kernel runs with MXFP8 data
+ *            together with the sheared bias; "vLLM TML Inkling サポート" lists
+ *            FP8 global attention as the way to relieve compute and the KV
+ *            cache.  MXFP8 is the OCP Microscaling Formats (MX) v1.0 format:
+ *            32 consecutive entries share a power-of-two E8M0 scale, entries
+ *            are FP8 E4M3 (OCP).
  *   [V-KV]   same page, section "vLLM テクニカル最適化": the serving engine keeps
  *            the caches of all layers in one unified KV cache manager, and
  *            multi-token prediction re-runs its heads over the accepted
@@ -68,11 +75,24 @@ typedef enum rba_dtype {
     RBA_BF16 = 1
 } rba_dtype;
 
+/* Storage of K and V ([S-FA4]). */
+typedef enum rba_kv_format {
+    RBA_KV_PLAIN = 0,   /* k, v have the element type dt */
+    RBA_KV_MXFP8 = 1    /* k, v hold OCP E4M3 codes (one byte each); k_scale, v_scale hold one
+                           E8M0 code per 32 head-dim entries (value 2^(code-127); code 255 is NaN).
+                           Attention then runs over the decoded values.  dt must be RBA_BF16. */
+} rba_kv_format;
+
 /* Shapes, pointers and options of one attention call (prefill or decode).
  *   q, o : [B, Sq, Hq, d]    strides q_s / o_s = {b, s, h}
  *   k, v : [B, Skv, Hkv, d]  strides k_s / v_s = {b, s, h}
  *   R    : [B, Sq, Hq, E]    strides R_s = {b, t, h}; NULL = no bias (E ignored)
- *   lse  : [B, Hq, Sq] fp32, contiguous; NULL = not written                     */
+ *   lse  : [B, Hq, Sq] fp32, contiguous; NULL = not written
+ *   kv_format = RBA_KV_MXFP8: k_scale, v_scale : [B, Skv, Hkv, d/32] bytes,
+ *          strides k_scale_s / v_scale_s = {b, s, h}, the d/32 codes of a row
+ *          contiguous (paged: laid out like the pools, {page, key, head}).
+ *          k_s / v_s are then byte strides and must be multiples of 16.
+ *   A zero-initialised tail (kv_format 0, scales NULL) is the plain format. */
 typedef struct rba_attn_args {
     rba_dtype dt;
     int B, Sq, Skv, Hq, Hkv, d, E;
@@ -84,6 +104,9 @@ typedef struct rba_attn_args {
     void *o;
     float *lse;
     int64_t q_s[3], k_s[3], v_s[3], o_s[3], R_s[3];
+    int kv_format;         /* rba_kv_format */
+    const void *k_scale, *v_scale;
+    int64_t k_scale_s[3], v_scale_s[3];
 } rba_attn_args;
 
 /* R = r . P per head  ([S-RPB], the relative-logit projection):
@@ -158,6 +181,20 @@ typedef struct rba_paged_kv {
  * verification (Sq > 1) over a paged cache.                                */
 rba_status rba_attn_paged(const rba_attn_args *args, const rba_paged_kv *kv, int num_splits, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/* MXFP8 encoding of `rows` vectors of n entries ([S-FA4]; the KV-cache
+ * write of an MXFP8 cache):
+ *   x      : [rows, n] in_dt (RBA_BF16 or RBA_FP32), row stride x_stride
+ *            elements; 16-byte aligned rows (x and x_stride * size)
+ *   codes  : [rows, n] bytes, row stride codes_stride (4-byte aligned rows)
+ *   scales : [rows, n/32] bytes, row stride scales_stride
+ * Block k of a row is entries [32k, 32k+32).  Its scale code is e + 127 with
+ * e = floor(log2(max |x|)) - 8 clamped to [-127, 127] (-127 for an all-zero
+ * block); each code is the E4M3 value nearest to x / 2^e, ties to even,
+ * saturated to +-448.  n a multiple of 32, 32 <= n <= 65536.  Inputs must
+ * be finite.  rows = 0 is a no-op.                                          */
+rba_status rba_mxfp8_quantize(rba_dtype in_dt, int64_t rows, int n, const void *x, int64_t x_stride, void *codes,
+                              int64_t codes_stride, void *scales, int64_t scales_stride, void *stream);
 
 /* Merge split partials into args->o (and args->lse if non-NULL):
  *   M = max_s lse_s;  w_s = exp(lse_s - M);  o = sum_s w_s o_s / sum_s w_s;

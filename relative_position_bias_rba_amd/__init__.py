@@ -19,7 +19,7 @@ import os
 import torch
 
 __all__ = [
-    "relproj", "attn_prefill", "attn_decode", "attn_paged", "splitkv_combine", "num_splits",
+    "relproj", "attn_prefill", "attn_decode", "attn_paged", "splitkv_combine", "num_splits", "mxfp8_quantize",
     "decode_workspace_bytes", "lib_path", "RBAError",
     "RBA_OK", "RBA_E_INVALID", "RBA_E_UNSUPPORTED", "RBA_E_WORKSPACE", "RBA_E_LAUNCH",
 ]
@@ -29,6 +29,7 @@ lib_path = os.path.join(_HERE, "librba.so")
 
 RBA_OK, RBA_E_INVALID, RBA_E_UNSUPPORTED, RBA_E_WORKSPACE, RBA_E_LAUNCH = range(5)
 RBA_FP32, RBA_BF16 = 0, 1
+RBA_KV_PLAIN, RBA_KV_MXFP8 = 0, 1
 
 
 class RBAError(RuntimeError):
@@ -51,6 +52,9 @@ class _AttnArgs(ctypes.Structure):
         ("lse", ctypes.c_void_p),
         ("q_s", ctypes.c_int64 * 3), ("k_s", ctypes.c_int64 * 3), ("v_s", ctypes.c_int64 * 3),
         ("o_s", ctypes.c_int64 * 3), ("R_s", ctypes.c_int64 * 3),
+        ("kv_format", ctypes.c_int),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("k_scale_s", ctypes.c_int64 * 3), ("v_scale_s", ctypes.c_int64 * 3),
     ]
 
 
@@ -88,6 +92,8 @@ def _load():
     lib.rba_splitkv_combine.restype = ci
     lib.rba_status_string.argtypes = [ci]
     lib.rba_status_string.restype = ctypes.c_char_p
+    lib.rba_mxfp8_quantize.argtypes = [ci, i64, ci, vp, i64, vp, i64, vp, i64, vp]
+    lib.rba_mxfp8_quantize.restype = ci
     lib.rba_calib_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
     lib.rba_calib_read.restype = ci
     lib.rba_calib_mfma.argtypes = [ci, vp, ctypes.POINTER(ctypes.c_double), vp]
@@ -122,8 +128,11 @@ def _ptr(t):
 
 
 def make_args(q, k, v, R=None, o=None, lse=None, *, window=0, scale=None, log_scale_base=0.0,
-              dt=None) -> _AttnArgs:
-    """Fill the C argument struct from tensors (shapes and strides only)."""
+              dt=None, k_scale=None, v_scale=None) -> _AttnArgs:
+    """Fill the C argument struct from tensors (shapes and strides only).
+
+    With k_scale / v_scale given, k and v are MXFP8 codes (uint8) and the
+    scales their E8M0 codes [..., 128/32]."""
     a = _AttnArgs()
     B, Sq, Hq, d = q.shape
     a.dt = _dt(q) if dt is None else dt
@@ -141,14 +150,28 @@ def make_args(q, k, v, R=None, o=None, lse=None, *, window=0, scale=None, log_sc
             if t.stride(3) != 1:
                 raise ValueError(f"{name[0]}: innermost dimension must be contiguous")
             getattr(a, name)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    if (k_scale is None) != (v_scale is None):
+        raise ValueError("give both k_scale and v_scale, or neither")
+    if k_scale is not None:
+        a.kv_format = RBA_KV_MXFP8
+        a.k_scale, a.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+        for name, t in (("k_scale_s", k_scale), ("v_scale_s", v_scale)):
+            if t.dtype != torch.uint8 or t.stride(3) != 1:
+                raise ValueError(f"{name}: uint8 with contiguous codes per row expected")
+            getattr(a, name)[:] = [t.stride(0), t.stride(1), t.stride(2)]
     return a
 
 
-def _check_attn_inputs(q, k, v, R):
-    for t in (q, k, v) + (() if R is None else (R,)):
+def _check_attn_inputs(q, k, v, R, k_scale=None, v_scale=None):
+    for t in (q, k, v) + (() if R is None else (R,)) + tuple(x for x in (k_scale, v_scale) if x is not None):
         if not t.is_cuda:
             raise ValueError("tensors must live on the GPU")
-    if k.dtype != q.dtype or v.dtype != q.dtype or (R is not None and R.dtype != q.dtype):
+    if R is not None and R.dtype != q.dtype:
+        raise TypeError("q and R must share one dtype")
+    if k_scale is not None:
+        if k.dtype != torch.uint8 or v.dtype != torch.uint8 or q.dtype != torch.bfloat16:
+            raise TypeError("MXFP8 K/V: k and v are uint8 codes and q is bfloat16")
+    elif k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v and R must share one dtype")
 
 
@@ -186,13 +209,15 @@ def relproj(r: torch.Tensor, P: torch.Tensor, out_dtype=None, per_head: bool = F
 
 
 def attn_prefill(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0, return_lse=False,
-                 out=None):
-    """Attention of every query row over its visible keys (one pass)."""
-    _check_attn_inputs(q, k, v, R)
+                 out=None, k_scale=None, v_scale=None):
+    """Attention of every query row over its visible keys (one pass).
+    k_scale / v_scale: K and V are MXFP8 (see mxfp8_quantize)."""
+    _check_attn_inputs(q, k, v, R, k_scale, v_scale)
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     lse = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=q.device) \
         if return_lse else None
-    a = make_args(q, k, v, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base)
+    a = make_args(q, k, v, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base,
+                  k_scale=k_scale, v_scale=v_scale)
     _check("rba_attn_prefill", _lib.rba_attn_prefill(ctypes.byref(a), _stream(q.device)))
     return (o, lse) if return_lse else o
 
@@ -208,13 +233,15 @@ def decode_workspace_bytes(q, k, v, R=None, *, window=0, splits=0) -> int:
 
 
 def attn_decode(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0, num_splits=0,
-                return_lse=False, out=None, workspace=None):
-    """Split-KV attention of a few query rows against a long KV cache."""
-    _check_attn_inputs(q, k, v, R)
+                return_lse=False, out=None, workspace=None, k_scale=None, v_scale=None):
+    """Split-KV attention of a few query rows against a long KV cache.
+    k_scale / v_scale: K and V are MXFP8 (see mxfp8_quantize)."""
+    _check_attn_inputs(q, k, v, R, k_scale, v_scale)
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     lse = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=q.device) \
         if return_lse else None
-    a = make_args(q, k, v, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base)
+    a = make_args(q, k, v, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base,
+                  k_scale=k_scale, v_scale=v_scale)
     splits = int(num_splits)
     if splits == 0:
         splits = _lib.rba_num_splits(ctypes.byref(a), 0)
@@ -246,14 +273,15 @@ def make_paged(block_table, seq_lens, page_size: int, num_pages: int) -> _PagedK
 
 
 def attn_paged(q, k_pool, v_pool, block_table, seq_lens, R=None, *, max_seq_len=None, window=0, scale=None,
-               log_scale_base=0.0, num_splits=0, return_lse=False, out=None, workspace=None):
+               log_scale_base=0.0, num_splits=0, return_lse=False, out=None, workspace=None, k_scale=None,
+               v_scale=None):
     """Attention of each sequence's last Sq query rows over its own keys in a
     paged pool k_pool / v_pool [num_pages, page_size, Hkv, 128].
 
     block_table int32 [B, n] (device) lists each sequence's pages; seq_lens
     int32 [B] (device) its key count.  max_seq_len (default n * page_size)
     bounds seq_lens and drives the split heuristic."""
-    _check_attn_inputs(q, k_pool, v_pool, R)
+    _check_attn_inputs(q, k_pool, v_pool, R, k_scale, v_scale)
     if not (block_table.is_cuda and seq_lens.is_cuda):
         raise ValueError("block_table and seq_lens must live on the GPU")
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
@@ -262,7 +290,8 @@ def attn_paged(q, k_pool, v_pool, block_table, seq_lens, R=None, *, max_seq_len=
     num_pages, page_size = k_pool.shape[0], k_pool.shape[1]
     if v_pool.shape[:2] != k_pool.shape[:2]:
         raise ValueError("k_pool and v_pool must have the same pages")
-    a = make_args(q, k_pool, v_pool, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base)
+    a = make_args(q, k_pool, v_pool, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base,
+                  k_scale=k_scale, v_scale=v_scale)
     a.Skv = int(block_table.shape[1] * page_size if max_seq_len is None else max_seq_len)
     kv = make_paged(block_table, seq_lens, page_size, num_pages)
     splits = int(num_splits)
@@ -278,6 +307,23 @@ def attn_paged(q, k_pool, v_pool, block_table, seq_lens, R=None, *, max_seq_len=
     code = _lib.rba_attn_paged(ctypes.byref(a), ctypes.byref(kv), splits, ws_ptr, ws_bytes, _stream(q.device))
     _check("rba_attn_paged", code)
     return (o, lse) if return_lse else o
+
+
+def mxfp8_quantize(x: torch.Tensor):
+    """MXFP8 codes and E8M0 scales of x [..., n] (n a multiple of 32) along its
+    last axis: (uint8 [..., n], uint8 [..., n/32])."""
+    if not x.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    n = x.shape[-1]
+    x2 = x.reshape(-1, n)
+    if x2.stride(1) != 1 or (x2.stride(0) * x2.element_size()) % 16 or x2.data_ptr() % 16:
+        x2 = x2.contiguous()
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(*x.shape[:-1], n // 32, dtype=torch.uint8, device=x.device)
+    code = _lib.rba_mxfp8_quantize(_dt(x), x2.shape[0], n, _ptr(x2), x2.stride(0), _ptr(codes), n,
+                                   _ptr(scales), n // 32, _stream(x.device))
+    _check("rba_mxfp8_quantize", code)
+    return codes, scales
 
 
 def splitkv_combine(o_part, lse_part, q_like, k_like, *, out=None, return_lse=False):

@@ -153,14 +153,33 @@ __device__ __forceinline__ void dma16_untracked(u32x4 rsrc, unsigned voff, const
                  : "memory", "m0");
 }
 
+// E8M0 scale code -> its power of two (code 0 is 2^-127, an fp32 subnormal).
+__device__ __forceinline__ float e8m0_scale(unsigned code) {
+    return __builtin_bit_cast(float, code == 0 ? 0x00400000u : code << 23);
+}
+
+// Four OCP E4M3 codes (bytes of w, lowest first) times 2^scale -> four bf16
+// in two dwords, lowest element in the low half.  Exact: an E4M3 value times
+// a power of two fits bf16 unless it leaves bf16's exponent range.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(unsigned w, float sc) {
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, sc, false);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, sc, true);
+    return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+}
+
 // PG: K and V live in a pool of fixed-size pages; key tile kt of sequence b
 // is read from page block_table[b][kt * N / page_size] (a page holds whole
 // tiles), and sequence b has its own length seq_lens[b].
-template <typename T, int NW, bool SLAB2, bool PG>
+// F8: K and V are MXFP8 (E4M3 codes, one E8M0 scale per 32 head-dim entries);
+// both go through registers, are decoded to bf16 exactly and stored in the
+// same LDS layouts as bf16 K and V, so the compute is the bf16 one.
+template <typename T, int NW, bool SLAB2, bool PG, bool F8>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnParams p) {
     using TL = Tile<T>;
     constexpr bool BF = sizeof(T) == 2;
+    static_assert(!F8 || BF, "MXFP8 K/V is decoded to bf16");
     constexpr int ES = (int)sizeof(T);
+    constexpr int KES = F8 ? 1 : ES;             // bytes per K/V element in memory
     constexpr int NTH = 64 * NW;                 // threads per workgroup
     constexpr int N = TL::N;
     constexpr int KT = N / 32;                   // 32-key sub-tiles per tile
@@ -217,9 +236,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     const int ncols = p.G * p.QB;
     const bool has_bias = p.R != nullptr && p.E > 0;
 
-    // paged: the page offset is added per tile
-    const T *__restrict__ gk = (const T *)p.k + (PG ? 0 : (int64_t)b * p.ks0) + (int64_t)hkv * p.ks2;
-    const T *__restrict__ gv = (const T *)p.v + (PG ? 0 : (int64_t)b * p.vs0) + (int64_t)hkv * p.vs2;
+    // byte addresses of this (batch, kv head)'s K/V rows; paged: the page
+    // offset is added per tile
+    const char *__restrict__ gk = (const char *)p.k + ((PG ? 0 : (int64_t)b * p.ks0) + (int64_t)hkv * p.ks2) * KES;
+    const char *__restrict__ gv = (const char *)p.v + ((PG ? 0 : (int64_t)b * p.vs0) + (int64_t)hkv * p.vs2) * KES;
+    const char *__restrict__ gks = F8 ? (const char *)p.k_scale + (PG ? 0 : (int64_t)b * p.kss0) + (int64_t)hkv * p.kss2
+                                      : nullptr;
+    const char *__restrict__ gvs = F8 ? (const char *)p.v_scale + (PG ? 0 : (int64_t)b * p.vss0) + (int64_t)hkv * p.vss2
+                                      : nullptr;
 
     // ------------------------------------------------------------ this lane's query column
     const int col = wave * 32 + lc;
@@ -288,9 +312,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     const int v_kq = (tid >> 2) & (NKQ - 1);
     const int v_dq = (tid & 3) | ((tid / (4 * NKQ)) << 2);
     unsigned vvo[NVI];
+    unsigned vso[F8 ? NVI : 1];                  // F8: the scale byte of each of those keys
 #pragma unroll
     for (int i = 0; i < NVI; ++i) {
-        if constexpr (BF) {
+        if constexpr (F8) {
+            vvo[i] = (unsigned)((int64_t)(NVI * v_kq + i) * p.vs1 + 4 * v_dq);
+            vso[i] = (unsigned)((int64_t)(NVI * v_kq + i) * p.vss1 + (v_dq >> 3));
+        } else if constexpr (BF) {
             vvo[i] = (unsigned)(((int64_t)(NVI * v_kq + i) * p.vs1 + 4 * v_dq) * ES);
         } else {
             const int ci = tid + NTH * i;
@@ -324,11 +352,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 
     typedef typename std::conditional<BF, u32x2, u32x4>::type VChunk;
     VChunk vreg[NVI];
+    // F8 staging registers: V codes (4 per key) and scale bytes; K as 16-byte
+    // pieces (16 codes of one key row, one scale) and their LDS destinations
+    constexpr int NK8 = F8 ? N * D / 16 / NTH : 1;   // K pieces per thread
+    unsigned v8[F8 ? NVI : 1], vsc[F8 ? NVI : 1];
+    u32x4 k8[NK8];
+    unsigned ksc[NK8], k8o[NK8], k8s[NK8], k8d[NK8];
+    if constexpr (F8) {
+#pragma unroll
+        for (int i = 0; i < NK8; ++i) {
+            const int L = i * NTH + tid;
+            const int row = L >> 3, c = L & 7;             // 8 pieces per 128-byte row
+            k8o[i] = (unsigned)((int64_t)row * p.ks1 + 16 * c);
+            k8s[i] = (unsigned)((int64_t)row * p.kss1 + (c >> 1));
+            k8d[i] = (unsigned)(lds_key_row(row) * KS + 16 * c);
+        }
+    }
 
     auto banded = [&](int kt) { return has_bias && (p_min - (kt * N + N - 1) < p.E); };
 
     // Rows j0 .. of K or V; rows past the sequence (or the page) read zeros.
-    auto kv_rsrc = [&](const T *g, int64_t pstride, int64_t stride, int j0) {
+    // Rows j0 .. of a per-key tensor at byte address g (strides in elements
+    // of esz bytes, rowbytes bytes per row); rows past the sequence (or the
+    // page) read zeros.
+    auto kv_rsrc = [&](const char *g, int64_t pstride, int64_t stride, int j0, int esz, int rowbytes) {
         if constexpr (PG) {
             const int pg = __builtin_amdgcn_readfirstlane(j0 / p.page_size);   // wave-uniform
             const int off = j0 - pg * p.page_size;
@@ -336,15 +383,39 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
             // vector-memory queue and make the tile's staging wait for it
             const int page = min(max(load_scalar(p.block_table + (int64_t)b * p.bt_stride + pg), 0), p.num_pages - 1);
             const int rows = min(p.page_size - off, Skv - j0);
-            return make_rsrc(g + (int64_t)page * pstride + (int64_t)off * stride,
-                             ((int64_t)(rows - 1) * stride + D) * ES);
+            return make_rsrc(g + ((int64_t)page * pstride + (int64_t)off * stride) * esz,
+                             (int64_t)(rows - 1) * stride * esz + rowbytes);
         } else {
-            return make_rsrc(g + (int64_t)j0 * stride, ((int64_t)(Skv - 1 - j0) * stride + D) * ES);
+            return make_rsrc(g + (int64_t)j0 * stride * esz, (int64_t)(Skv - 1 - j0) * stride * esz + rowbytes);
+        }
+    };
+
+    // F8: K codes and scales of tile kt into registers
+    auto load_k8 = [&](int kt) {
+        const rsrc_t rk = kv_rsrc(gk, p.ks0, p.ks1, kt * N, 1, D);
+        const rsrc_t rs = kv_rsrc(gks, p.kss0, p.kss1, kt * N, 1, D / 32);
+#pragma unroll
+        for (int i = 0; i < NK8; ++i) {
+            k8[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k8o[i], 0, 0);
+            ksc[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, k8s[i], 0, 0);
+        }
+    };
+
+    // F8: decode the K registers into K buffer buf (bf16, the DMA layout)
+    auto store_k8 = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NK8; ++i) {
+            const float sc = e8m0_scale(ksc[i]);
+            const u32x2 a = e4m3x4_to_bf16(k8[i][0], sc), b2 = e4m3x4_to_bf16(k8[i][1], sc);
+            const u32x2 c = e4m3x4_to_bf16(k8[i][2], sc), d = e4m3x4_to_bf16(k8[i][3], sc);
+            T *dst = &sK[buf][k8d[i]];
+            *(u32x4 *)dst = u32x4{a[0], a[1], b2[0], b2[1]};
+            *(u32x4 *)(dst + 8) = u32x4{c[0], c[1], d[0], d[1]};
         }
     };
 
     auto stage_k = [&](int kt, int buf) {
-        const rsrc_t rk = kv_rsrc(gk, p.ks0, p.ks1, kt * N);
+        const rsrc_t rk = kv_rsrc(gk, p.ks0, p.ks1, kt * N, ES, D * ES);
 #pragma unroll
         for (int i = 0; i < NKI; ++i) {
             const int wc = (i * NW + wave) * 64;
@@ -353,7 +424,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     };
 
     auto load_v = [&](int kt) {
-        const rsrc_t rv = kv_rsrc(gv, p.vs0, p.vs1, kt * N);
+        if constexpr (F8) {
+            const rsrc_t rv = kv_rsrc(gv, p.vs0, p.vs1, kt * N, 1, D);
+            const rsrc_t rs = kv_rsrc(gvs, p.vss0, p.vss1, kt * N, 1, D / 32);
+#pragma unroll
+            for (int i = 0; i < NVI; ++i) {
+                v8[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vvo[i], 0, 0);
+                vsc[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, vso[i], 0, 0);
+            }
+            return;
+        }
+        const rsrc_t rv = kv_rsrc(gv, p.vs0, p.vs1, kt * N, ES, D * ES);
 #pragma unroll
         for (int i = 0; i < NVI; ++i) {
             if constexpr (BF)
@@ -364,6 +445,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     };
 
     auto store_v = [&]() {
+        if constexpr (F8) {
+#pragma unroll
+            for (int i = 0; i < NVI; ++i) vreg[i] = e4m3x4_to_bf16(v8[i], e8m0_scale(vsc[i]));
+        }
         if constexpr (BF) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -610,9 +695,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 
     int kt = n_it > 0 ? next_tile() : 0;
     if (n_it > 0) {
-        stage_k(kt, 0);
+        if constexpr (F8)
+            load_k8(kt);
+        else
+            stage_k(kt, 0);
         load_v(kt);
         if (banded(kt)) stage_slab(kt, 0);
+        if constexpr (F8) store_k8(0);
         store_v();
         wait_vmem();
     }
@@ -623,7 +712,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         const int kn = nxt ? next_tile() : kt;
         const bool slab_ahead = !SLAB2 && nxt && r_dma && banded(kn) && !banded(kt);
         if (nxt) {
-            stage_k(kn, cur ^ 1);
+            if constexpr (F8)
+                load_k8(kn);
+            else
+                stage_k(kn, cur ^ 1);
             if (slab_ahead) stage_slab_ahead(kn);
             load_v(kn);
             if (SLAB2 && banded(kn)) stage_slab(kn, cur ^ 1);
@@ -632,6 +724,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         wait_vmem();
         __syncthreads();             // tile kt fully consumed; loads for kn landed
         if (nxt) {
+            if constexpr (F8) store_k8(cur ^ 1);
             store_v();
             if (!SLAB2 && banded(kn) && !slab_ahead) {
                 stage_slab(kn, 0);
@@ -1245,28 +1338,42 @@ hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stre
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
     const bool paged = p.block_table != nullptr;
+    const bool f8 = p.k_scale != nullptr;
+    // K/V in plain bf16 or fp32 (the pp kernel needs 32-bit K/V offsets), or MXFP8
+#define RBA_FWD(T, NW, SLAB2, PG, F8)                                                                   \
+    hipLaunchKernelGGL((attn_fwd_kernel<T, NW, SLAB2, PG, F8>), grid, dim3(64 * NW), 0, stream, p)
     switch (v) {
         case AttnVariant::BF16_WIDE:    // 8 waves, 256 columns
-            if (paged)
-                hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 8, true, true>), grid, dim3(512), 0, stream, p);
-            else if (p.kv32)            // two ping-pong groups (32-bit K/V offsets)
+            if (f8 && paged)
+                RBA_FWD(__bf16, 8, true, true, true);
+            else if (f8)
+                RBA_FWD(__bf16, 8, true, false, true);
+            else if (paged)
+                RBA_FWD(__bf16, 8, true, true, false);
+            else if (p.kv32)            // two ping-pong groups
                 hipLaunchKernelGGL(attn_prefill_pp_kernel, grid, dim3(512), 0, stream, p);
             else
-                hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 8, true, false>), grid, dim3(512), 0, stream, p);
+                RBA_FWD(__bf16, 8, true, false, false);
             break;
         case AttnVariant::BF16_NARROW:  // 4 waves: 128 columns, small LDS footprint
-            if (paged)
-                hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 4, false, true>), grid, dim3(256), 0, stream, p);
+            if (f8 && paged)
+                RBA_FWD(__bf16, 4, false, true, true);
+            else if (f8)
+                RBA_FWD(__bf16, 4, false, false, true);
+            else if (paged)
+                RBA_FWD(__bf16, 4, false, true, false);
             else
-                hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 4, false, false>), grid, dim3(256), 0, stream, p);
+                RBA_FWD(__bf16, 4, false, false, false);
             break;
-        case AttnVariant::FP32:
+        case AttnVariant::FP32:         // MXFP8 K/V is bf16-only (rejected by the caller)
+            if (f8) return hipErrorInvalidValue;
             if (paged)
-                hipLaunchKernelGGL((attn_fwd_kernel<float, 4, false, true>), grid, dim3(256), 0, stream, p);
+                RBA_FWD(float, 4, false, true, false);
             else
-                hipLaunchKernelGGL((attn_fwd_kernel<float, 4, false, false>), grid, dim3(256), 0, stream, p);
+                RBA_FWD(float, 4, false, false, false);
             break;
     }
+#undef RBA_FWD
     return hipGetLastError();
 }
 

@@ -28,9 +28,14 @@ bool strides_ok(const int64_t s[3], int64_t mult) {
     return true;
 }
 
+// Bytes per K/V element in memory.
+int kv_elem_size(const rba_attn_args *a) { return a->kv_format == RBA_KV_MXFP8 ? 1 : elem_size(a->dt); }
+
 rba_status validate_attn(const rba_attn_args *a) {
     if (a == nullptr) return RBA_E_INVALID;
     if (a->dt != RBA_BF16 && a->dt != RBA_FP32) return RBA_E_UNSUPPORTED;
+    if (a->kv_format != RBA_KV_PLAIN && a->kv_format != RBA_KV_MXFP8) return RBA_E_INVALID;
+    if (a->kv_format == RBA_KV_MXFP8 && a->dt != RBA_BF16) return RBA_E_UNSUPPORTED;
     if (a->d <= 0) return RBA_E_INVALID;
     if (a->d != kHeadDim) return RBA_E_UNSUPPORTED;
     if (a->B < 0 || a->Sq < 0 || a->Skv < 0 || a->Hq < 1 || a->Hkv < 1) return RBA_E_INVALID;
@@ -48,8 +53,13 @@ rba_status validate_attn(const rba_attn_args *a) {
     if (a->q == nullptr || a->k == nullptr || a->v == nullptr || a->o == nullptr) return RBA_E_INVALID;
     if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->o, 16)) return RBA_E_INVALID;
     const int64_t ch = 16 / elem_size(a->dt);
-    if (!strides_ok(a->q_s, ch) || !strides_ok(a->k_s, ch) || !strides_ok(a->v_s, ch) || !strides_ok(a->o_s, ch))
+    const int64_t kch = 16 / kv_elem_size(a);
+    if (!strides_ok(a->q_s, ch) || !strides_ok(a->k_s, kch) || !strides_ok(a->v_s, kch) || !strides_ok(a->o_s, ch))
         return RBA_E_INVALID;
+    if (a->kv_format == RBA_KV_MXFP8) {
+        if (a->k_scale == nullptr || a->v_scale == nullptr) return RBA_E_INVALID;
+        if (!strides_ok(a->k_scale_s, 1) || !strides_ok(a->v_scale_s, 1)) return RBA_E_INVALID;
+    }
     if (a->R != nullptr) {
         if (!aligned(a->R, elem_size(a->dt))) return RBA_E_INVALID;
         if (!strides_ok(a->R_s, 1)) return RBA_E_INVALID;
@@ -135,6 +145,13 @@ rba::AttnParams make_params(const rba_attn_args *a, const Plan &pl, int splits) 
               a->R_s[1] % ch == 0 && a->R_s[2] % ch == 0;
     const int64_t kv_row = std::max(a->k_s[1], a->v_s[1]);
     p.kv32 = ((int64_t)a->Skv * kv_row + kHeadDim) * elem_size(a->dt) < ((int64_t)1 << 31);
+    if (a->kv_format == RBA_KV_MXFP8) {
+        p.kv32 = 0;   // the MXFP8 path is the register-staged kernel
+        p.k_scale = (const uint8_t *)a->k_scale;
+        p.v_scale = (const uint8_t *)a->v_scale;
+        p.kss0 = a->k_scale_s[0], p.kss1 = a->k_scale_s[1], p.kss2 = a->k_scale_s[2];
+        p.vss0 = a->v_scale_s[0], p.vss1 = a->v_scale_s[1], p.vss2 = a->v_scale_s[2];
+    }
     return p;
 }
 
@@ -229,7 +246,7 @@ rba_status rba_attn_paged(const rba_attn_args *args, const rba_paged_kv *kv, int
         return RBA_E_INVALID;
     // one page of K or V must lie within a 32-bit buffer range
     const int64_t kv_row = std::max(args->k_s[1], args->v_s[1]);
-    if (((int64_t)(kv->page_size - 1) * kv_row + kHeadDim) * elem_size(args->dt) >= ((int64_t)1 << 31))
+    if (((int64_t)(kv->page_size - 1) * kv_row + kHeadDim) * kv_elem_size(args) >= ((int64_t)1 << 31))
         return RBA_E_UNSUPPORTED;
     const Plan pl = make_plan(args);
     if (num_splits == 0) {
@@ -266,6 +283,21 @@ rba_status rba_splitkv_combine(const float *o_part, const float *lse_part, int n
     const hipError_t e =
         rba::launch_combine(o_part, lse_part, num_splits, args->B, args->Sq, args->Hq, args->o, args->dt == RBA_BF16,
                             args->o_s[0], args->o_s[1], args->o_s[2], args->lse, (hipStream_t)stream);
+    return e == hipSuccess ? RBA_OK : RBA_E_LAUNCH;
+}
+
+rba_status rba_mxfp8_quantize(rba_dtype in_dt, int64_t rows, int n, const void *x, int64_t x_stride, void *codes,
+                              int64_t codes_stride, void *scales, int64_t scales_stride, void *stream) {
+    if (in_dt != RBA_BF16 && in_dt != RBA_FP32) return RBA_E_UNSUPPORTED;
+    if (rows < 0 || n < 32 || n % 32 != 0 || n > 65536) return RBA_E_INVALID;
+    if (rows == 0) return RBA_OK;
+    if (x == nullptr || codes == nullptr || scales == nullptr) return RBA_E_INVALID;
+    const int es = elem_size(in_dt);
+    if (!aligned(x, 16) || (x_stride * es) % 16 != 0 || x_stride < n) return RBA_E_INVALID;
+    if (!aligned(codes, 4) || codes_stride % 4 != 0 || codes_stride < n) return RBA_E_INVALID;
+    if (scales_stride < n / 32) return RBA_E_INVALID;
+    const hipError_t e = rba::launch_mxfp8_quantize(in_dt == RBA_BF16, rows, n, x, x_stride, codes, codes_stride,
+                                                    scales, scales_stride, (hipStream_t)stream);
     return e == hipSuccess ? RBA_OK : RBA_E_LAUNCH;
 }
 

@@ -34,6 +34,12 @@ struct AttnParams {
     int64_t bt_stride;
     int page_size;
     int num_pages;
+    // MXFP8 K/V (k_scale != null): k and v hold E4M3 codes (one byte per
+    // element, strides ks*/vs* in bytes) and k_scale / v_scale one E8M0 byte
+    // per 32 head-dim entries, [.., key, head, 4] with strides kss* / vss*
+    // (bytes) laid out like k and v (paged: page, key, head).
+    const uint8_t *k_scale, *v_scale;
+    int64_t kss0, kss1, kss2, vss0, vss1, vss2;
 };
 
 // Kernel variants.  WIDE: two 32-column tiles per wave (prefill, bf16).
@@ -50,6 +56,9 @@ hipError_t launch_combine(const float *o_part, const float *lse_part, int splits
 
 hipError_t launch_relproj(bool in_bf16, bool out_bf16, int64_t T, int Hq, int r_dim, int E, const void *r,
                           int64_t r_stride, int64_t r_stride_h, const void *P, void *R, hipStream_t stream);
+
+hipError_t launch_mxfp8_quantize(bool in_bf16, int64_t rows, int n, const void *x, int64_t x_stride, void *codes,
+                                 int64_t codes_stride, void *scales, int64_t scales_stride, hipStream_t stream);
 
 hipError_t launch_calib_read(const void *buf, int64_t bytes, void *sink, int blocks, hipStream_t stream);
 

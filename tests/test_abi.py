@@ -25,6 +25,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("rba_relproj", "rba_attn_prefill", "rba_attn_decode", "rba_attn_paged", "rba_splitkv_combine",
+                 "rba_mxfp8_quantize",
                  "rba_num_splits", "rba_decode_workspace_bytes", "rba_status_string"):
         assert must in names
 
@@ -180,6 +181,46 @@ def test_paged_empty_is_noop():
     kv.block_table = None
     kv.seq_lens = None
     assert _paged_call(a, kv, splits=3) == RBA_OK
+
+
+def test_mxfp8_kv_validation():
+    q, k, v, R, o = _tensors()
+    kc = torch.zeros(k.shape, dtype=torch.uint8)
+    ks = torch.zeros(*k.shape[:3], 4, dtype=torch.uint8)
+    a = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks)
+    assert a.kv_format == rba.RBA_KV_MXFP8
+    a2 = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks); a2.kv_format = 2
+    assert _prefill(a2) == RBA_E_INVALID
+    a2 = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks); a2.dt = 0
+    assert _prefill(a2) == RBA_E_UNSUPPORTED and _decode(a2) == RBA_E_UNSUPPORTED
+    a2 = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks); a2.k_scale = None
+    assert _prefill(a2) == RBA_E_INVALID
+    a2 = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks); a2.k_s[1] = 136   # bytes, not a 16-multiple
+    assert _prefill(a2) == RBA_E_INVALID
+    a2 = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks); a2.v_scale_s[0] = -4
+    assert _decode(a2) == RBA_E_INVALID
+    with pytest.raises(ValueError):
+        make_args(q, kc, kc, R, o, k_scale=ks)
+
+
+def test_mxfp8_quantize_validation():
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    c = torch.zeros(4, 128, dtype=torch.uint8)
+    sc = torch.zeros(4, 4, dtype=torch.uint8)
+    px, pc, ps = (ctypes.c_void_p(t.data_ptr()) for t in (x, c, sc))
+    f = lib.rba_mxfp8_quantize
+    assert f(1, 0, 128, None, 128, None, 128, None, 4, None) == RBA_OK
+    assert f(1, 4, 48, px, 128, pc, 128, ps, 4, None) == RBA_E_INVALID          # n not a multiple of 32
+    assert f(1, 4, 0, px, 128, pc, 128, ps, 4, None) == RBA_E_INVALID
+    assert f(1, -1, 128, px, 128, pc, 128, ps, 4, None) == RBA_E_INVALID
+    assert f(1, 4, 128, px, 100, pc, 128, ps, 4, None) == RBA_E_INVALID         # x rows overlap
+    assert f(1, 4, 128, px, 132, pc, 128, ps, 4, None) == RBA_E_INVALID         # x rows not 16-byte aligned
+    assert f(1, 4, 128, ctypes.c_void_p(x.data_ptr() + 8), 128, pc, 128, ps, 4, None) == RBA_E_INVALID
+    assert f(1, 4, 128, px, 128, pc, 126, ps, 4, None) == RBA_E_INVALID
+    assert f(1, 4, 128, px, 128, ctypes.c_void_p(c.data_ptr() + 2), 128, ps, 4, None) == RBA_E_INVALID
+    assert f(1, 4, 128, px, 128, pc, 128, ps, 3, None) == RBA_E_INVALID
+    assert f(1, 4, 128, px, 128, pc, 128, None, 4, None) == RBA_E_INVALID
+    assert f(5, 4, 128, px, 128, pc, 128, ps, 4, None) == RBA_E_UNSUPPORTED
 
 
 def test_calib_validation():
