@@ -145,10 +145,12 @@ def cpu_baseline(w, inp, budget_s=15.0):
                       f"from r and P), {t_used:.1f} s"}
 
 
-def decode_leg(rba, torch, name, reps):
+def decode_leg(rba, torch, name, reps, mxfp8=False):
+    """One decode workload; mxfp8: its K/V cache encoded to MXFP8 by the library's
+    encoder (timed too) and attention run over the encoded cache."""
     from workloads import CONFIGS, make_inputs
     w = CONFIGS[name]
-    log(f"decode {name}: generating inputs")
+    log(f"decode {name}{' mxfp8' if mxfp8 else ''}: generating inputs")
     inp = make_inputs(w)
     d = {k: v.to("cuda") for k, v in inp.items()}
     del inp
@@ -157,16 +159,43 @@ def decode_leg(rba, torch, name, reps):
     o = torch.empty_like(d["q"])
     need = rba.decode_workspace_bytes(d["q"], d["k"], d["v"], R, window=w.window, splits=splits)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-    a = rba.make_args(d["q"], d["k"], d["v"], R, o, None, window=w.window, log_scale_base=w.log_scale_base)
+    st = rba._stream(d["q"].device)
+    extra = {}
+    kv_bytes = w.kv_bytes()
+    if mxfp8:
+        x = d["k"].reshape(-1, w.d)
+        kc = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+        ksc = torch.empty(x.shape[0], w.d // 32, dtype=torch.uint8, device="cuda")
+        enc = c_launcher(rba, "rba_mxfp8_quantize", 1, x.shape[0], w.d, ctypes.c_void_p(x.data_ptr()), w.d,
+                         ctypes.c_void_p(kc.data_ptr()), w.d, ctypes.c_void_p(ksc.data_ptr()), w.d // 32, st)
+        ms_enc = time_launches(enc, reps, torch)
+        enc_bytes = x.numel() * 2 + kc.numel() + ksc.numel()
+        extra["encode_k"] = {"ms": round(ms_enc, 4), "GBps": round(enc_bytes / (ms_enc * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(enc_bytes / (ms_enc * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "bytes": enc_bytes}
+        k8, ks = rba.mxfp8_quantize(d["k"])
+        v8, vs = rba.mxfp8_quantize(d["v"])
+        del d["k"], d["v"], x, kc, ksc
+        torch.cuda.empty_cache()
+        a = rba.make_args(d["q"], k8, v8, R, o, None, window=w.window, log_scale_base=w.log_scale_base,
+                          k_scale=ks, v_scale=vs)
+        kv_bytes = kv_bytes * (w.d + w.d // 32) // (2 * w.d)     # codes + scales per bf16 pair of bytes
+        keep = (k8, ks, v8, vs)
+    else:
+        a = rba.make_args(d["q"], d["k"], d["v"], R, o, None, window=w.window, log_scale_base=w.log_scale_base)
+        keep = ()
     launch = c_launcher(rba, "rba_attn_decode", ctypes.byref(a), splits, ctypes.c_void_p(ws.data_ptr()),
-                        ws.numel(), rba._stream(d["q"].device))
+                        ws.numel(), st)
     ms_warm = time_launches(launch, reps, torch)
     ms = time_cold(launch, max(reps, 50), torch)
-    gbs = w.kv_bytes() / (ms * 1e-3) / 1e9
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
     res = {"ms": round(ms, 4), "kv_GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-           "ms_warm": round(ms_warm, 4), "num_splits": splits, "kv_bytes": w.kv_bytes(),
+           "ms_warm": round(ms_warm, 4), "num_splits": splits, "kv_bytes": kv_bytes,
            "timing": "median of 50 launches, each after a 512 MiB read that evicts the caches; ms_warm: back-to-back mean"}
-    del d, R, o, ws
+    if mxfp8:
+        res["kv_format"] = "MXFP8 (E4M3 codes + E8M0 scale per 32 head-dim entries)"
+    res.update(extra)
+    del d, R, o, ws, keep
     torch.cuda.empty_cache()
     return res
 
@@ -335,6 +364,8 @@ def main():
         for name in ("c4_decode_swa", "c4_decode_full", "c5_long_decode"):
             out["decode"][name] = decode_leg(rba, torch, name, 20)
         out["decode"]["c4_decode_full_paged64"] = paged_decode_leg(rba, torch, "c4_decode_full", 64, 20, 8192)
+        for name in ("c4_decode_full", "c5_long_decode"):
+            out["decode"][name + "_mxfp8"] = decode_leg(rba, torch, name, 20, mxfp8=True)
     att = attainable(rba, torch)
     out["attainable"] = att
     out["roofline"]["frac_attainable"] = round(out["roofline"]["achieved"] / att["mfma_bf16_TFLOPs"], 4)

@@ -196,11 +196,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     constexpr int KCH = N * CPRP;                // K chunks per tile incl. padding
     constexpr int NKI = (KCH + NTH - 1) / NTH;   // K DMA instructions per thread
     constexpr int NVI = BF ? N * D / (NTH * 4) : N * CPR / NTH;  // V loads per thread
-    constexpr int NSB = SLAB2 ? 2 : 1;
+    constexpr int NSB = (SLAB2 || F8) ? 2 : 1;
     static_assert(NVI * NTH * (BF ? 4 : CH) == N * D, "V tile must split evenly over threads");
 
-    __shared__ __attribute__((aligned(16))) T sK[2][N * KS];
-    __shared__ __attribute__((aligned(16))) T sV[TL::VROWS * VS];
+    // F8: one K and one V buffer (registers carry the tiles in flight); V is
+    // row-major with 16-byte chunks XOR-swizzled by row and read transposed
+    constexpr int NKB = F8 ? 1 : 2;
+    constexpr int VSZ = F8 ? N * D : TL::VROWS * VS;
+    __shared__ __attribute__((aligned(16))) T sK[NKB][N * KS];
+    __shared__ __attribute__((aligned(16))) T sV[VSZ];
     __shared__ __attribute__((aligned(16))) T sR[NSB][SROWS * SW];
 
     const int tid = threadIdx.x;
@@ -311,14 +315,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     constexpr int NKQ = BF ? N / NVI : 1;        // key groups (bf16)
     const int v_kq = (tid >> 2) & (NKQ - 1);
     const int v_dq = (tid & 3) | ((tid / (4 * NKQ)) << 2);
-    unsigned vvo[NVI];
-    unsigned vso[F8 ? NVI : 1];                  // F8: the scale byte of each of those keys
+    unsigned vvo[F8 ? 1 : NVI];
 #pragma unroll
-    for (int i = 0; i < NVI; ++i) {
-        if constexpr (F8) {
-            vvo[i] = (unsigned)((int64_t)(NVI * v_kq + i) * p.vs1 + 4 * v_dq);
-            vso[i] = (unsigned)((int64_t)(NVI * v_kq + i) * p.vss1 + (v_dq >> 3));
-        } else if constexpr (BF) {
+    for (int i = 0; i < (F8 ? 0 : NVI); ++i) {
+        if constexpr (BF) {
             vvo[i] = (unsigned)(((int64_t)(NVI * v_kq + i) * p.vs1 + 4 * v_dq) * ES);
         } else {
             const int ci = tid + NTH * i;
@@ -352,21 +352,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 
     typedef typename std::conditional<BF, u32x2, u32x4>::type VChunk;
     VChunk vreg[NVI];
-    // F8 staging registers: V codes (4 per key) and scale bytes; K as 16-byte
-    // pieces (16 codes of one key row, one scale) and their LDS destinations
-    constexpr int NK8 = F8 ? N * D / 16 / NTH : 1;   // K pieces per thread
-    unsigned v8[F8 ? NVI : 1], vsc[F8 ? NVI : 1];
-    u32x4 k8[NK8];
-    unsigned ksc[NK8], k8o[NK8], k8s[NK8], k8d[NK8];
+    // F8 staging: each thread moves NP8 16-byte pieces (16 codes of one key
+    // row, under one scale) of K and of V per tile.  Piece L is piece L % 8 of
+    // key row L / 8.  Two register sets carry the next two tiles.
+    constexpr int NP8 = F8 ? N * D / 16 / NTH : 1;
+    struct F8Set {
+        u32x4 k[NP8], v[NP8];
+        unsigned ks[NP8], vs[NP8];
+    };
+    // Offsets of piece 0; piece i is NTH / 8 rows further (the row
+    // permutation and the chunk swizzle do not change over 32 rows).
+    constexpr int RSTEP = NTH / 8;
+    unsigned k8o = 0, k8s = 0, k8d = 0, v8o = 0, v8s = 0, v8d = 0;
     if constexpr (F8) {
-#pragma unroll
-        for (int i = 0; i < NK8; ++i) {
-            const int L = i * NTH + tid;
-            const int row = L >> 3, c = L & 7;             // 8 pieces per 128-byte row
-            k8o[i] = (unsigned)((int64_t)row * p.ks1 + 16 * c);
-            k8s[i] = (unsigned)((int64_t)row * p.kss1 + (c >> 1));
-            k8d[i] = (unsigned)(lds_key_row(row) * KS + 16 * c);
-        }
+        const int row = tid >> 3, c = tid & 7;
+        k8o = (unsigned)((int64_t)row * p.ks1 + 16 * c);
+        k8s = (unsigned)((int64_t)row * p.kss1 + (c >> 1));
+        k8d = (unsigned)(lds_key_row(row) * KS + 16 * c);
+        v8o = (unsigned)((int64_t)row * p.vs1 + 16 * c);
+        v8s = (unsigned)((int64_t)row * p.vss1 + (c >> 1));
+        // bf16 chunks 2c, 2c+1 of row r sit at chunks (2c) ^ 4(r % 4) and the next
+        v8d = (unsigned)(row * D + 8 * ((2 * c) ^ ((row & 3) << 2)));
     }
 
     auto banded = [&](int kt) { return has_bias && (p_min - (kt * N + N - 1) < p.E); };
@@ -390,25 +396,37 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         }
     };
 
-    // F8: K codes and scales of tile kt into registers
-    auto load_k8 = [&](int kt) {
+    // F8: codes and scales of tile kt's K and V into register set X
+    auto load8 = [&](int kt, F8Set &X) __attribute__((always_inline)) {
         const rsrc_t rk = kv_rsrc(gk, p.ks0, p.ks1, kt * N, 1, D);
-        const rsrc_t rs = kv_rsrc(gks, p.kss0, p.kss1, kt * N, 1, D / 32);
+        const rsrc_t rks = kv_rsrc(gks, p.kss0, p.kss1, kt * N, 1, D / 32);
+        const rsrc_t rv = kv_rsrc(gv, p.vs0, p.vs1, kt * N, 1, D);
+        const rsrc_t rvs = kv_rsrc(gvs, p.vss0, p.vss1, kt * N, 1, D / 32);
 #pragma unroll
-        for (int i = 0; i < NK8; ++i) {
-            k8[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k8o[i], 0, 0);
-            ksc[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, k8s[i], 0, 0);
+        for (int i = 0; i < NP8; ++i) {
+            const unsigned r = (unsigned)(i * RSTEP);
+            X.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k8o + r * (unsigned)p.ks1, 0, 0);
+            X.ks[i] = __builtin_amdgcn_raw_buffer_load_b8(rks, k8s + r * (unsigned)p.kss1, 0, 0);
+            X.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v8o + r * (unsigned)p.vs1, 0, 0);
+            X.vs[i] = __builtin_amdgcn_raw_buffer_load_b8(rvs, v8s + r * (unsigned)p.vss1, 0, 0);
         }
     };
+    // vector-memory instructions one load8 issues
+    constexpr int kLoad8Ops = 4 * NP8;
 
-    // F8: decode the K registers into K buffer buf (bf16, the DMA layout)
-    auto store_k8 = [&](int buf) {
+    // F8: decode register set X into the K and V buffers (bf16)
+    auto store8 = [&](const F8Set &X) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < NK8; ++i) {
-            const float sc = e8m0_scale(ksc[i]);
-            const u32x2 a = e4m3x4_to_bf16(k8[i][0], sc), b2 = e4m3x4_to_bf16(k8[i][1], sc);
-            const u32x2 c = e4m3x4_to_bf16(k8[i][2], sc), d = e4m3x4_to_bf16(k8[i][3], sc);
-            T *dst = &sK[buf][k8d[i]];
+        for (int i = 0; i < NP8; ++i) {
+            const float sk = e8m0_scale(X.ks[i]), sv = e8m0_scale(X.vs[i]);
+            u32x2 a = e4m3x4_to_bf16(X.k[i][0], sk), b2 = e4m3x4_to_bf16(X.k[i][1], sk);
+            u32x2 c = e4m3x4_to_bf16(X.k[i][2], sk), d = e4m3x4_to_bf16(X.k[i][3], sk);
+            T *dst = &sK[0][k8d + i * RSTEP * KS];
+            *(u32x4 *)dst = u32x4{a[0], a[1], b2[0], b2[1]};
+            *(u32x4 *)(dst + 8) = u32x4{c[0], c[1], d[0], d[1]};
+            a = e4m3x4_to_bf16(X.v[i][0], sv), b2 = e4m3x4_to_bf16(X.v[i][1], sv);
+            c = e4m3x4_to_bf16(X.v[i][2], sv), d = e4m3x4_to_bf16(X.v[i][3], sv);
+            dst = &sV[v8d + i * RSTEP * D];
             *(u32x4 *)dst = u32x4{a[0], a[1], b2[0], b2[1]};
             *(u32x4 *)(dst + 8) = u32x4{c[0], c[1], d[0], d[1]};
         }
@@ -424,16 +442,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     };
 
     auto load_v = [&](int kt) {
-        if constexpr (F8) {
-            const rsrc_t rv = kv_rsrc(gv, p.vs0, p.vs1, kt * N, 1, D);
-            const rsrc_t rs = kv_rsrc(gvs, p.vss0, p.vss1, kt * N, 1, D / 32);
-#pragma unroll
-            for (int i = 0; i < NVI; ++i) {
-                v8[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vvo[i], 0, 0);
-                vsc[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, vso[i], 0, 0);
-            }
-            return;
-        }
         const rsrc_t rv = kv_rsrc(gv, p.vs0, p.vs1, kt * N, ES, D * ES);
 #pragma unroll
         for (int i = 0; i < NVI; ++i) {
@@ -445,10 +453,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     };
 
     auto store_v = [&]() {
-        if constexpr (F8) {
-#pragma unroll
-            for (int i = 0; i < NVI; ++i) vreg[i] = e4m3x4_to_bf16(v8[i], e8m0_scale(vsc[i]));
-        }
         if constexpr (BF) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -511,12 +515,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     // tile before it is computed (that tile then carries no bias, so the
     // buffer is free).  Untracked so that the compiler does not hold the LDS
     // reads of that compute until it lands; the end-of-iteration wait does.
-    auto stage_slab_ahead = [&](int kt) {
+    auto stage_slab_ahead = [&](int kt, int buf) {
         const unsigned eoff = (unsigned)(-kt * N * ES);
 #pragma unroll
         for (int i = 0; i < NSI; ++i) {
             const int wc = (i * NW + wave) * 64;
-            if (i < NSI - 1 || wc + lane < SCH) dma16_untracked(rR4, svo[i] + eoff, &sR[0][wc * CH]);
+            if (i < NSI - 1 || wc + lane < SCH) dma16_untracked(rR4, svo[i] + eoff, &sR[buf][wc * CH]);
         }
     };
 
@@ -524,6 +528,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     const int kr0 = lds_key_row(mfma_row_key(lc));   // LDS row of this lane's A-operand key (+32: sub-tile 1)
     const T *k_lane = &sK[0][kr0 * KS];
     const T *v_lane = BF ? &sV[lc * VS + 16 * hh] : &sV[16 * hh * VS + lc];
+    // F8 (row-major V): V^T fragment of PV step (u, h2, dt) by two transpose
+    // reads of 4 keys each.  Lane (g = lane / 16, a = lane % 4, i = lane / 4 % 4)
+    // addresses key row 32u + 16(g / 2) + 8h2 + 4x + i and head-dim entries
+    // 32dt + 16(g % 2) + 4a, and receives key rows of one head-dim entry back.
+    const int tr_i = (lane >> 2) & 3;
+    const int vt_base = (16 * hh + tr_i) * D + CH * ((((lane >> 4) & 1) << 1) | ((lane >> 1) & 1)) + 4 * (lane & 1);
+    auto vt_off = [&](int dt) __attribute__((always_inline)) { return vt_base + CH * (((dt ^ tr_i) << 2)); };
     const int s_lane = col * SW + (prow - rb) - 16 * hh;   // slab entry of key offset 16*hh
 
     auto compute_tile = [&](int kt, int buf, int sbuf) {
@@ -644,7 +655,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
                                                               bf16x2{(__bf16)1.f, (__bf16)1.f}, sum, false);
 #pragma unroll
                     for (int dt = 0; dt < 4; ++dt) {
-                        const bf16x8 a = *(const bf16x8 *)(v_lane + 32 * dt * VS + 32 * u + 8 * h2);
+                        bf16x8 a;
+                        if constexpr (F8) {
+                            typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                            const T *base = &sV[vt_off(dt) + (32 * u + 8 * h2) * D];
+                            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                (__attribute__((address_space(3))) bf16x4_t *)base);
+                            const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                (__attribute__((address_space(3))) bf16x4_t *)(base + 4 * D));
+                            a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        } else {
+                            a = *(const bf16x8 *)(v_lane + 32 * dt * VS + 32 * u + 8 * h2);
+                        }
                         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, O[dt], 0, 0, 0);
                     }
                 }
@@ -694,29 +716,70 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     };
 
     int kt = n_it > 0 ? next_tile() : 0;
-    if (n_it > 0) {
-        if constexpr (F8)
-            load_k8(kt);
-        else
-            stage_k(kt, 0);
+    if constexpr (F8) {
+        // Two tiles in flight: while tile kt is computed from LDS, the codes of
+        // tile kn wait in one register set and those of the tile after it load
+        // into the other; each iteration decodes kn into the (single) K and V
+        // buffers between two barriers.  Bias windows are double-buffered and
+        // go by direct-to-LDS loads issued before the next codes, so a counted
+        // wait lands them without waiting for the codes.
+        F8Set A, B;
+        int kn = n_it > 1 ? next_tile() : kt;
+        if (n_it > 0) {
+            load8(kt, A);
+            if (n_it > 1) load8(kn, B);
+            if (banded(kt)) stage_slab(kt, 0);
+            store8(A);
+            wait_vmem();
+        }
+        __syncthreads();
+        auto body = [&](int it, F8Set &X, F8Set &Y) __attribute__((always_inline)) {
+            const bool nxt = it + 1 < n_it, nxt2 = it + 2 < n_it;
+            const int kn2 = nxt2 ? next_tile() : kn;
+            const int sb = it & 1;                       // bias buffer of kt; kn's is sb ^ 1
+            const bool sdma = nxt && r_dma && banded(kn);
+            if (sdma) stage_slab_ahead(kn, sb ^ 1);
+            if (nxt2) load8(kn2, Y);
+            if (wave_active) compute_tile(kt, 0, sb);
+            if (sdma) {
+                if (nxt2)
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoad8Ops) : "memory");
+                else
+                    wait_vmem();
+            }
+            __syncthreads();                             // kt consumed; kn's bias landed
+            if (nxt) {
+                store8(X);
+                if (!r_dma && banded(kn)) {
+                    stage_slab(kn, sb ^ 1);
+                    wait_vmem();
+                }
+            }
+            __syncthreads();
+            kt = kn;
+            kn = kn2;
+        };
+        for (int it = 0; it < n_it; it += 2) {
+            body(it, B, A);
+            if (it + 1 < n_it) body(it + 1, A, B);
+        }
+    }
+    if (!F8 && n_it > 0) {
+        stage_k(kt, 0);
         load_v(kt);
         if (banded(kt)) stage_slab(kt, 0);
-        if constexpr (F8) store_k8(0);
         store_v();
         wait_vmem();
     }
-    __syncthreads();
-    for (int it = 0; it < n_it; ++it) {
+    if (!F8) __syncthreads();
+    for (int it = 0; it < (F8 ? 0 : n_it); ++it) {
         const int cur = it & 1;
         const bool nxt = it + 1 < n_it;
         const int kn = nxt ? next_tile() : kt;
         const bool slab_ahead = !SLAB2 && nxt && r_dma && banded(kn) && !banded(kt);
         if (nxt) {
-            if constexpr (F8)
-                load_k8(kn);
-            else
-                stage_k(kn, cur ^ 1);
-            if (slab_ahead) stage_slab_ahead(kn);
+            stage_k(kn, cur ^ 1);
+            if (slab_ahead) stage_slab_ahead(kn, 0);
             load_v(kn);
             if (SLAB2 && banded(kn)) stage_slab(kn, cur ^ 1);
         }
@@ -724,7 +787,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         wait_vmem();
         __syncthreads();             // tile kt fully consumed; loads for kn landed
         if (nxt) {
-            if constexpr (F8) store_k8(cur ^ 1);
             store_v();
             if (!SLAB2 && banded(kn) && !slab_ahead) {
                 stage_slab(kn, 0);
