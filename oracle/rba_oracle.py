@@ -23,6 +23,14 @@ prose only; no listing, worked example or numbers exist for this path):
   [V-ARCH] "vLLM TML Inkling サポート" (agentlenshq.com), section
            "TML Inkling モデルアーキテクチャ": GQA with head size 128 in every
            layer; the relative term is added to the logits before softmax.
+  [S-SC]   "SGLang と Miles が Inkling を初日からサポート", sections "Inkling の
+           モデルアーキテクチャ", "ShortConv：4カ所に現れる短距離因果畳み込み" and
+           "ShortConv 最適化": ShortConv is a per-channel causal convolution
+           along the tokens that reads the current token and the W-1 before
+           it (W = 4); in attention it runs on the K stream after the K
+           projection and before the Q/K normalisation, and on the V stream
+           after the V projection; SGLang fuses the K/V convolutions, the Q/K
+           RMSNorm and the KV-cache write into one attention-prologue kernel.
   [V-KV]   same page, section "vLLM テクニカル最適化": the serving engine
            keeps the caches of all layers in one unified KV cache manager and
            re-runs the multi-token-prediction heads over accepted tokens.
@@ -53,6 +61,14 @@ design notes):
     x / 2^e rounded to the nearest E4M3 value, ties to even, saturated to
     +-448.  K and V are blocked along the head dimension (32 entries), and
     attention with an MXFP8 cache is the attention over the decoded values.
+  * Attention prologue ([S-SC]): ShortConv tap i multiplies the row i
+    positions back (tap 0 = the current token), no bias, no activation;
+    positions before a sequence's start read zero.  RMSNorm is
+    x / sqrt(mean(x^2) + eps) * g over the 128 entries of one head, with one
+    weight vector g per stream (q or k) shared by the heads.  K is
+    normalised after its convolution; V is convolved only; Q is normalised
+    only.  The conv state of a sequence holds the pre-convolution rows of
+    its last W-1 positions.
   * Paged cache ([V-KV]): sequence b has its own length L_b; its key j is row
     j % page_size of page block_table[b][j // page_size] of a shared pool;
     its Sq query rows are its last Sq positions, L_b - Sq + t.
@@ -83,6 +99,9 @@ __all__ = [
     "gather_pages",
     "attention_paged",
     "e4m3_value",
+    "short_conv",
+    "rms_norm",
+    "attention_prologue",
     "mxfp8_quantize",
     "mxfp8_dequantize",
 ]
@@ -432,3 +451,75 @@ def mxfp8_dequantize(codes, scales):
     vals = e4m3_value(codes).reshape(*codes.shape[:-1], n // MX_BLOCK, MX_BLOCK)
     s = np.where(scales == 255, np.nan, np.ldexp(1.0, scales - 127))
     return (vals * s[..., None]).reshape(codes.shape)
+
+
+# --------------------------------------------------------------------------- attention prologue ([S-SC])
+
+def short_conv(x, w, history):
+    """Causal per-channel convolution of one sequence's new rows.
+
+    x [n, C] new pre-convolution rows; history [W-1, C] the pre-convolution
+    rows of the W-1 positions before them, oldest first (rows for positions
+    before the sequence start must be zero); w [C, W], tap i multiplies the
+    row i positions back.  Returns y [n, C] with
+    y[t, c] = sum_i w[c, i] * x_ext[t - i, c]."""
+    x, w, history = _f64(x), _f64(w), _f64(history)
+    W = w.shape[1]
+    ext = np.concatenate([history.reshape(W - 1, -1), x], axis=0)   # row W-1+t is x[t]
+    n = x.shape[0]
+    y = np.zeros_like(x)
+    for i in range(W):
+        y += w[:, i][None, :] * ext[W - 1 - i:W - 1 - i + n]
+    return y
+
+
+def rms_norm(x, g, eps):
+    """x / sqrt(mean(x^2) + eps) * g along the last axis."""
+    x, g = _f64(x), _f64(g)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
+
+
+def attention_prologue(q, k, v, cu_new, seq_lens, wk, wv, gq, gk, eps, state_k, state_v):
+    """The attention prologue for T new tokens of B sequences.
+
+    q [T, Hq, d], k/v [T, Hkv, d]: projections of the new tokens, sequence b
+    owning rows cu_new[b] .. cu_new[b+1]-1, which sit at positions
+    seq_lens[b] - n_b ... seq_lens[b] - 1 (n_b = its new-token count);
+    wk/wv [Hkv*d, W] conv taps; gq/gk [d] RMSNorm weights; state_k/state_v
+    [B, W-1, Hkv, d] pre-convolution rows of each sequence's last W-1
+    positions before this call (oldest first).
+
+    Returns q_out [T, Hq, d] (RMSNorm of q), k_rows [T, Hkv, d] (RMSNorm of
+    the convolved k), v_rows [T, Hkv, d] (convolved v), pos [T] (cache
+    position of each row), new_state_k, new_state_v."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    state_k, state_v = _f64(state_k), _f64(state_v)
+    cu = [int(x) for x in cu_new]
+    T, Hkv, d = k.shape
+    B = len(cu) - 1
+    W = np.asarray(wk).shape[1]
+    q_out = rms_norm(q, gq, eps)
+    k_rows = np.zeros_like(k)
+    v_rows = np.zeros_like(v)
+    pos = np.zeros(T, dtype=np.int64)
+    nsk, nsv = state_k.copy(), state_v.copy()
+    for b in range(B):
+        a, e = cu[b], cu[b + 1]
+        n = e - a
+        L = int(seq_lens[b])
+        start = L - n                               # position of the first new token
+        hk, hv = state_k[b].copy(), state_v[b].copy()     # [W-1, Hkv, d]
+        for j in range(W - 1):                     # history rows before position 0 read zero
+            if start - (W - 1) + j < 0:
+                hk[j] = 0.0
+                hv[j] = 0.0
+        yk = short_conv(k[a:e].reshape(n, -1), wk, hk.reshape(W - 1, -1)).reshape(n, Hkv, d)
+        yv = short_conv(v[a:e].reshape(n, -1), wv, hv.reshape(W - 1, -1)).reshape(n, Hkv, d)
+        k_rows[a:e] = rms_norm(yk, gk, eps)
+        v_rows[a:e] = yv
+        pos[a:e] = start + np.arange(n)
+        ext_k = np.concatenate([state_k[b], k[a:e]], axis=0)   # positions start-(W-1) ... L-1
+        ext_v = np.concatenate([state_v[b], v[a:e]], axis=0)
+        nsk[b] = ext_k[-(W - 1):]
+        nsv[b] = ext_v[-(W - 1):]
+    return q_out, k_rows, v_rows, pos, nsk, nsv

@@ -18,6 +18,7 @@ import torch
 from oracle import (attention, attention_paged, attention_partial, attention_rows, brute_attention,
                     e4m3_value, gather_pages, log_scale_factor, lse_combine, mxfp8_dequantize, mxfp8_quantize,
                     relproj)
+from oracle import attention_prologue, rms_norm, short_conv
 from oracle.rba_oracle import _e4m3_encode
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
@@ -490,3 +491,91 @@ def test_mxfp8_error_bound_and_brute_force():
                 if v <= 448:
                     q = 2.0 ** (max(np.floor(np.log2(v)) if v > 0 else -6, -6) - 3)
                     assert abs(d[r, 32 * k + i] - blk[i]) <= 0.5 * q * 2.0 ** e * (1 + 1e-12)
+
+
+# --------------------------------------------------------------------------- attention prologue
+
+def test_short_conv_taps_identity_shift_and_brute_force():
+    rng = np.random.default_rng(21)
+    n, C, W = 6, 5, 4
+    x = rng.standard_normal((n, C))
+    hist = rng.standard_normal((W - 1, C))
+    w = np.zeros((C, W))
+    w[:, 0] = 1.0
+    assert np.array_equal(short_conv(x, w, hist), x)                 # tap 0 is the current row
+    w = np.zeros((C, W))
+    w[:, 2] = 1.0                                                     # two rows back
+    y = short_conv(x, w, hist)
+    assert np.array_equal(y[2:], x[:-2]) and np.array_equal(y[:2], hist[1:])
+    w = rng.standard_normal((C, W))
+    y = short_conv(x, w, hist)
+    rows = list(hist) + list(x)
+    for t in range(n):
+        for c in range(C):
+            want = 0.0
+            for i in range(W):
+                want += w[c, i] * rows[W - 1 + t - i][c]
+            assert abs(y[t, c] - want) <= 1e-12
+
+
+def test_rms_norm_closed_forms():
+    g = np.linspace(0.5, 2.0, 8)
+    x = np.full((3, 8), 2.0)
+    y = rms_norm(x, g, 0.0)
+    assert np.allclose(y, np.broadcast_to(g, (3, 8)), rtol=0, atol=1e-15)   # constant rows -> g
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((4, 128))
+    y = rms_norm(x, np.ones(128), 0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=0, atol=1e-12)
+    assert np.allclose(rms_norm(7.5 * x, np.ones(128), 0.0), y, rtol=0, atol=1e-12)   # scale invariant
+    eps = 0.3
+    y = rms_norm(np.ones((1, 4)), np.ones(4), eps)
+    assert np.allclose(y, 1.0 / np.sqrt(1.0 + eps), rtol=0, atol=1e-15)
+
+
+def _prologue_case(seed, lens_new, lens_total, Hq=4, Hkv=2, d=8, W=4):
+    rng = np.random.default_rng(seed)
+    T = sum(lens_new)
+    B = len(lens_new)
+    cu = np.concatenate([[0], np.cumsum(lens_new)])
+    q = rng.standard_normal((T, Hq, d))
+    k = rng.standard_normal((T, Hkv, d))
+    v = rng.standard_normal((T, Hkv, d))
+    wk = rng.standard_normal((Hkv * d, W))
+    wv = rng.standard_normal((Hkv * d, W))
+    gq = rng.standard_normal(d)
+    gk = rng.standard_normal(d)
+    sk = rng.standard_normal((B, W - 1, Hkv, d))
+    sv = rng.standard_normal((B, W - 1, Hkv, d))
+    return q, k, v, cu, np.array(lens_total), wk, wv, gq, gk, sk, sv
+
+
+def test_prologue_split_into_two_calls_equals_one():
+    q, k, v, cu, L, wk, wv, gq, gk, sk, sv = _prologue_case(23, [5, 3], [12, 3])
+    full = attention_prologue(q, k, v, cu, L, wk, wv, gq, gk, 1e-6, sk, sv)
+    # first call: 2 and 1 new tokens; second call: the remaining 3 and 2
+    idx1 = [0, 1, 5]
+    idx2 = [2, 3, 4, 6, 7]
+    p1 = attention_prologue(q[idx1], k[idx1], v[idx1], [0, 2, 3], [9, 1], wk, wv, gq, gk, 1e-6, sk, sv)
+    p2 = attention_prologue(q[idx2], k[idx2], v[idx2], [0, 3, 5], [12, 3], wk, wv, gq, gk, 1e-6, p1[4], p1[5])
+    for out in (0, 1, 2):
+        got = np.zeros_like(full[out])
+        got[idx1] = p1[out]
+        got[idx2] = p2[out]
+        assert np.allclose(got, full[out], rtol=0, atol=1e-12)
+    assert np.array_equal(np.concatenate([p1[3], p2[3]])[np.argsort(idx1 + idx2)], full[3])
+    assert np.allclose(p2[4], full[4]) and np.allclose(p2[5], full[5])
+
+
+def test_prologue_sequence_start_ignores_history_and_places_rows():
+    # sequence 1 starts at position 0 (3 new tokens, length 3): its state must not matter
+    q, k, v, cu, L, wk, wv, gq, gk, sk, sv = _prologue_case(24, [2, 3], [10, 3])
+    a = attention_prologue(q, k, v, cu, L, wk, wv, gq, gk, 1e-6, sk, sv)
+    sk2, sv2 = sk.copy(), sv.copy()
+    sk2[1] = 1e3
+    sv2[1] = -1e3
+    b = attention_prologue(q, k, v, cu, L, wk, wv, gq, gk, 1e-6, sk2, sv2)
+    assert np.array_equal(a[1][2:], b[1][2:]) and np.array_equal(a[2][2:], b[2][2:])
+    assert list(a[3]) == [8, 9, 0, 1, 2]
+    # V of the first row of sequence 1 is tap 0 times the row itself
+    assert np.allclose(a[2][2], wv[:, 0].reshape(2, 8) * v[2], rtol=0, atol=1e-12)
