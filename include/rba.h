@@ -23,6 +23,12 @@
  *            cache.  MXFP8 is the OCP Microscaling Formats (MX) v1.0 format:
  *            32 consecutive entries share a power-of-two E8M0 scale, entries
  *            are FP8 E4M3 (OCP).
+ *   [S-SC]   "SGLang と Miles が Inkling を初日からサポート", sections
+ *            "ShortConv：4カ所に現れる短距離因果畳み込み" and "ShortConv 最適化": a
+ *            per-channel causal convolution over the current token and the
+ *            W-1 before it (W = 4) runs on the K stream before the Q/K
+ *            normalisation and on the V stream; the convolutions, the Q/K
+ *            RMSNorm and the KV-cache write are one prologue kernel.
  *   [V-KV]   same page, section "vLLM テクニカル最適化": the serving engine keeps
  *            the caches of all layers in one unified KV cache manager, and
  *            multi-token prediction re-runs its heads over the accepted
@@ -195,6 +201,51 @@ rba_status rba_attn_paged(const rba_attn_args *args, const rba_paged_kv *kv, int
  * be finite.  rows = 0 is a no-op.                                          */
 rba_status rba_mxfp8_quantize(rba_dtype in_dt, int64_t rows, int n, const void *x, int64_t x_stride, void *codes,
                               int64_t codes_stride, void *scales, int64_t scales_stride, void *stream);
+
+/* Attention prologue ([S-SC]): for T new tokens of B sequences, in one pass,
+ *   q_out[t, h]            = RMSNorm(q[t, h]; norm_q)
+ *   cache K row (b, pos, g) = RMSNorm(ShortConv_k(k)[t, g]; norm_k)
+ *   cache V row (b, pos, g) = ShortConv_v(v)[t, g]
+ * with ShortConv(x)[t, g, c] = sum_{i < conv_w} w[g*d + c][i] * x at the
+ * position i before t of the same sequence (tap 0 = the token itself; rows
+ * before the sequence start read zero; rows before this call's new tokens
+ * come from the conv state) and RMSNorm(x; w) = x * w / sqrt(mean(x^2) + eps)
+ * over the d entries of one head.  Sequence b owns token rows
+ * cu_new[b] .. cu_new[b+1]-1 (n_b of them), which take cache positions
+ * seq_lens[b] - n_b .. seq_lens[b] - 1.  Afterwards the conv state of each
+ * sequence holds the pre-convolution k and v rows of its last conv_w - 1
+ * positions.
+ *   cu_new     : device int32 [B+1], non-decreasing, cu_new[0] = 0, cu_new[B] = T
+ *   seq_lens   : device int32 [B], keys after this append (clamped on the
+ *                device to [n_b, cache->Skv])
+ *   q, k, v    : bf16 [T, Hq|Hkv, d], strides {token, head} (elements, multiples of 4)
+ *   conv_wk/wv : fp32 [Hkv*d, conv_w] contiguous;  norm_q/norm_k : fp32 [d]
+ *   state_k/v  : bf16 [B, conv_w - 1, Hkv, d] contiguous, read and updated
+ *                (NULL allowed when conv_w = 1)
+ *   q_out      : bf16 [T, Hq, d], strides {token, head}
+ * The cache is described exactly as rba_attn_decode reads it: `cache` gives
+ * k, v, k_s, v_s, Hkv, Skv, d, kv_format and (MXFP8) the scales; its other
+ * fields are ignored.  MXFP8 caches receive the bf16 row encoded as by
+ * rba_mxfp8_quantize.  `paged` (NULL = dense [B, Skv, Hkv, d]) selects a
+ * block-table cache as for rba_attn_paged.  d = 128, 1 <= conv_w <= 8,
+ * eps > 0.  T = 0 is a no-op.                                              */
+typedef struct rba_prologue_args {
+    int B, T, Hq, Hkv, d;
+    int conv_w;
+    float eps;
+    const int32_t *cu_new;
+    const int32_t *seq_lens;
+    const void *q, *k, *v;
+    int64_t q_s[2], k_s[2], v_s[2];
+    const float *conv_wk, *conv_wv;
+    const float *norm_q, *norm_k;
+    void *state_k, *state_v;
+    void *q_out;
+    int64_t q_out_s[2];
+} rba_prologue_args;
+
+rba_status rba_attn_prologue(const rba_prologue_args *args, const rba_attn_args *cache, const rba_paged_kv *paged,
+                             void *stream);
 
 /* Merge split partials into args->o (and args->lse if non-NULL):
  *   M = max_s lse_s;  w_s = exp(lse_s - M);  o = sum_s w_s o_s / sum_s w_s;

@@ -465,7 +465,7 @@ def short_conv(x, w, history):
     y[t, c] = sum_i w[c, i] * x_ext[t - i, c]."""
     x, w, history = _f64(x), _f64(w), _f64(history)
     W = w.shape[1]
-    ext = np.concatenate([history.reshape(W - 1, -1), x], axis=0)   # row W-1+t is x[t]
+    ext = np.concatenate([history.reshape(W - 1, x.shape[1]), x], axis=0)   # row W-1+t is x[t]
     n = x.shape[0]
     y = np.zeros_like(x)
     for i in range(W):
@@ -513,13 +513,14 @@ def attention_prologue(q, k, v, cu_new, seq_lens, wk, wv, gq, gk, eps, state_k, 
             if start - (W - 1) + j < 0:
                 hk[j] = 0.0
                 hv[j] = 0.0
-        yk = short_conv(k[a:e].reshape(n, -1), wk, hk.reshape(W - 1, -1)).reshape(n, Hkv, d)
-        yv = short_conv(v[a:e].reshape(n, -1), wv, hv.reshape(W - 1, -1)).reshape(n, Hkv, d)
+        yk = short_conv(k[a:e].reshape(n, Hkv * d), wk, hk.reshape(W - 1, Hkv * d)).reshape(n, Hkv, d)
+        yv = short_conv(v[a:e].reshape(n, Hkv * d), wv, hv.reshape(W - 1, Hkv * d)).reshape(n, Hkv, d)
         k_rows[a:e] = rms_norm(yk, gk, eps)
         v_rows[a:e] = yv
         pos[a:e] = start + np.arange(n)
-        ext_k = np.concatenate([state_k[b], k[a:e]], axis=0)   # positions start-(W-1) ... L-1
-        ext_v = np.concatenate([state_v[b], v[a:e]], axis=0)
-        nsk[b] = ext_k[-(W - 1):]
-        nsv[b] = ext_v[-(W - 1):]
+        if W > 1:
+            ext_k = np.concatenate([state_k[b], k[a:e]], axis=0)   # positions start-(W-1) ... L-1
+            ext_v = np.concatenate([state_v[b], v[a:e]], axis=0)
+            nsk[b] = ext_k[len(ext_k) - (W - 1):]
+            nsv[b] = ext_v[len(ext_v) - (W - 1):]
     return q_out, k_rows, v_rows, pos, nsk, nsv

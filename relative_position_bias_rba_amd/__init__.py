@@ -20,6 +20,7 @@ import torch
 
 __all__ = [
     "relproj", "attn_prefill", "attn_decode", "attn_paged", "splitkv_combine", "num_splits", "mxfp8_quantize",
+    "attn_prologue", "cache_args",
     "decode_workspace_bytes", "lib_path", "RBAError",
     "RBA_OK", "RBA_E_INVALID", "RBA_E_UNSUPPORTED", "RBA_E_WORKSPACE", "RBA_E_LAUNCH",
 ]
@@ -68,6 +69,22 @@ class _PagedKV(ctypes.Structure):
     ]
 
 
+class _PrologueArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int), ("T", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("d", ctypes.c_int),
+        ("conv_w", ctypes.c_int),
+        ("eps", ctypes.c_float),
+        ("cu_new", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("q_s", ctypes.c_int64 * 2), ("k_s", ctypes.c_int64 * 2), ("v_s", ctypes.c_int64 * 2),
+        ("conv_wk", ctypes.c_void_p), ("conv_wv", ctypes.c_void_p),
+        ("norm_q", ctypes.c_void_p), ("norm_k", ctypes.c_void_p),
+        ("state_k", ctypes.c_void_p), ("state_v", ctypes.c_void_p),
+        ("q_out", ctypes.c_void_p),
+        ("q_out_s", ctypes.c_int64 * 2),
+    ]
+
+
 def _load():
     if not os.path.exists(lib_path):
         raise ImportError(
@@ -88,6 +105,8 @@ def _load():
     lib.rba_attn_decode.restype = ci
     lib.rba_attn_paged.argtypes = [P, ctypes.POINTER(_PagedKV), ci, vp, ctypes.c_size_t, vp]
     lib.rba_attn_paged.restype = ci
+    lib.rba_attn_prologue.argtypes = [ctypes.POINTER(_PrologueArgs), P, ctypes.POINTER(_PagedKV), vp]
+    lib.rba_attn_prologue.restype = ci
     lib.rba_splitkv_combine.argtypes = [vp, vp, ci, P, vp]
     lib.rba_splitkv_combine.restype = ci
     lib.rba_status_string.argtypes = [ci]
@@ -324,6 +343,66 @@ def mxfp8_quantize(x: torch.Tensor):
                                    _ptr(scales), n // 32, _stream(x.device))
     _check("rba_mxfp8_quantize", code)
     return codes, scales
+
+
+def cache_args(k_cache, v_cache, *, k_scale=None, v_scale=None, max_seq_len=None) -> _AttnArgs:
+    """The C description of a KV cache alone (dense [B, Skv, Hkv, d] or a page
+    pool [num_pages, page_size, Hkv, d]; bf16, or MXFP8 codes with scales)."""
+    a = _AttnArgs()
+    a.dt, a.d, a.Hkv = RBA_BF16, k_cache.shape[3], k_cache.shape[2]
+    a.Skv = k_cache.shape[1] if max_seq_len is None else int(max_seq_len)
+    a.k, a.v = k_cache.data_ptr(), v_cache.data_ptr()
+    a.k_s[:] = [k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)]
+    a.v_s[:] = [v_cache.stride(0), v_cache.stride(1), v_cache.stride(2)]
+    if k_scale is not None:
+        a.kv_format = RBA_KV_MXFP8
+        a.k_scale, a.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+        a.k_scale_s[:] = [k_scale.stride(0), k_scale.stride(1), k_scale.stride(2)]
+        a.v_scale_s[:] = [v_scale.stride(0), v_scale.stride(1), v_scale.stride(2)]
+    return a
+
+
+def attn_prologue(q, k, v, cu_new, seq_lens, conv_wk, conv_wv, norm_q, norm_k, state_k, state_v, k_cache, v_cache,
+                  *, eps=1e-6, k_scale=None, v_scale=None, block_table=None, max_seq_len=None, q_out=None):
+    """Attention prologue for T new tokens: returns q_out = RMSNorm(q) and writes
+    RMSNorm(ShortConv(k)) and ShortConv(v) into the cache at each sequence's new
+    positions, then advances the conv states (see rba.h for the layouts).
+    block_table (int32 [B, n]) makes k_cache / v_cache page pools."""
+    T, Hq, d = q.shape
+    W = conv_wk.shape[1]
+    for t in (q, k, v, cu_new, seq_lens, conv_wk, conv_wv, norm_q, norm_k, k_cache, v_cache):
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("projections are bfloat16")
+    for t in (conv_wk, conv_wv, norm_q, norm_k):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError("conv taps and norm weights are contiguous float32")
+    out = torch.empty(T, Hq, d, dtype=torch.bfloat16, device=q.device) if q_out is None else q_out
+    a = _PrologueArgs()
+    a.B, a.T, a.Hq, a.Hkv, a.d, a.conv_w, a.eps = seq_lens.shape[0], T, Hq, k.shape[1], d, W, float(eps)
+    a.cu_new, a.seq_lens = cu_new.data_ptr(), seq_lens.data_ptr()
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    for name, t in (("q_s", q), ("k_s", k), ("v_s", v), ("q_out_s", out)):
+        if t.stride(2) != 1:
+            raise ValueError(f"{name}: innermost dimension must be contiguous")
+        getattr(a, name)[:] = [t.stride(0), t.stride(1)]
+    a.conv_wk, a.conv_wv = conv_wk.data_ptr(), conv_wv.data_ptr()
+    a.norm_q, a.norm_k = norm_q.data_ptr(), norm_k.data_ptr()
+    a.state_k = None if state_k is None else state_k.data_ptr()
+    a.state_v = None if state_v is None else state_v.data_ptr()
+    a.q_out = out.data_ptr()
+    if block_table is not None:
+        ms = block_table.shape[1] * k_cache.shape[1] if max_seq_len is None else max_seq_len
+        c = cache_args(k_cache, v_cache, k_scale=k_scale, v_scale=v_scale, max_seq_len=ms)
+        kv = make_paged(block_table, seq_lens, k_cache.shape[1], k_cache.shape[0])
+        kvp = ctypes.byref(kv)
+    else:
+        c = cache_args(k_cache, v_cache, k_scale=k_scale, v_scale=v_scale)
+        kvp = None
+    code = _lib.rba_attn_prologue(ctypes.byref(a), ctypes.byref(c), kvp, _stream(q.device))
+    _check("rba_attn_prologue", code)
+    return out
 
 
 def splitkv_combine(o_part, lse_part, q_like, k_like, *, out=None, return_lse=False):

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librba.so")
-SOURCES = ["rba_abi.cpp", "attn_kernels.hip", "relproj_kernels.hip", "quant_kernels.hip",
+SOURCES = ["rba_abi.cpp", "attn_kernels.hip", "relproj_kernels.hip", "quant_kernels.hip", "prologue_kernels.hip",
            "calib_kernels.hip"]
 
 

@@ -16,7 +16,8 @@ constexpr int kHeadDim = 128;
 constexpr int kMaxSplits = 1024;
 constexpr int kMinTilesPerSplit = 4;
 constexpr int kPageQuantum = 64;   // paged K/V: a page holds whole 64-key tiles
-constexpr size_t kCalibReadQuantum = 16384;   // the read probe covers 1024 16-byte chunks per step
+constexpr size_t kCalibReadQuantum = 16384;
+constexpr int kMaxConvTaps = 8;   // the read probe covers 1024 16-byte chunks per step
 
 int elem_size(rba_dtype dt) { return dt == RBA_BF16 ? 2 : 4; }
 
@@ -270,6 +271,71 @@ rba_status rba_attn_paged(const rba_attn_args *args, const rba_paged_kv *kv, int
     p.lse_part = p.o_part + (size_t)num_splits * rows * kHeadDim;
     if (rba::launch_attention(p, pl.var, s) != hipSuccess) return RBA_E_LAUNCH;
     return rba_splitkv_combine(p.o_part, p.lse_part, num_splits, args, stream);
+}
+
+rba_status rba_attn_prologue(const rba_prologue_args *a, const rba_attn_args *c, const rba_paged_kv *kv,
+                             void *stream) {
+    if (a == nullptr || c == nullptr) return RBA_E_INVALID;
+    if (c->dt != RBA_BF16) return RBA_E_UNSUPPORTED;
+    if (c->kv_format != RBA_KV_PLAIN && c->kv_format != RBA_KV_MXFP8) return RBA_E_INVALID;
+    if (a->d != kHeadDim || c->d != kHeadDim) return a->d <= 0 ? RBA_E_INVALID : RBA_E_UNSUPPORTED;
+    if (a->B < 0 || a->T < 0 || a->Hq < 1 || a->Hkv < 1 || a->Hkv != c->Hkv || c->Skv < 1) return RBA_E_INVALID;
+    if (a->conv_w < 1 || a->conv_w > kMaxConvTaps) return RBA_E_INVALID;
+    if (!isfinite(a->eps) || !(a->eps > 0.f)) return RBA_E_INVALID;
+    if (a->T == 0) return RBA_OK;
+    if (a->B < 1) return RBA_E_INVALID;
+    if (a->cu_new == nullptr || a->seq_lens == nullptr || a->q == nullptr || a->k == nullptr || a->v == nullptr ||
+        a->conv_wk == nullptr || a->conv_wv == nullptr || a->norm_q == nullptr || a->norm_k == nullptr ||
+        a->q_out == nullptr || c->k == nullptr || c->v == nullptr)
+        return RBA_E_INVALID;
+    if (a->conv_w > 1 && (a->state_k == nullptr || a->state_v == nullptr)) return RBA_E_INVALID;
+    // 8-byte pieces of bf16 rows
+    auto rows_ok = [](const void *p, const int64_t *s, int n) {
+        if (!aligned(p, 8)) return false;
+        for (int i = 0; i < n; ++i)
+            if (s[i] < 0 || s[i] % 4 != 0) return false;
+        return true;
+    };
+    if (!rows_ok(a->q, a->q_s, 2) || !rows_ok(a->k, a->k_s, 2) || !rows_ok(a->v, a->v_s, 2) ||
+        !rows_ok(a->q_out, a->q_out_s, 2) || !rows_ok(c->k, c->k_s, 3) || !rows_ok(c->v, c->v_s, 3))
+        return RBA_E_INVALID;
+    if (a->conv_w > 1 && (!aligned(a->state_k, 8) || !aligned(a->state_v, 8))) return RBA_E_INVALID;
+    if (!aligned(a->cu_new, 4) || !aligned(a->seq_lens, 4) || !aligned(a->conv_wk, 4) || !aligned(a->conv_wv, 4) ||
+        !aligned(a->norm_q, 4) || !aligned(a->norm_k, 4))
+        return RBA_E_INVALID;
+    const bool f8 = c->kv_format == RBA_KV_MXFP8;
+    if (f8 && (c->k_scale == nullptr || c->v_scale == nullptr || !strides_ok(c->k_scale_s, 1) ||
+               !strides_ok(c->v_scale_s, 1)))
+        return RBA_E_INVALID;
+    if (kv != nullptr) {
+        if (kv->page_size < kPageQuantum || kv->page_size % kPageQuantum != 0 || kv->num_pages < 1)
+            return RBA_E_INVALID;
+        if (kv->bt_stride < ((int64_t)c->Skv + kv->page_size - 1) / kv->page_size) return RBA_E_INVALID;
+        if (kv->block_table == nullptr || !aligned(kv->block_table, 4)) return RBA_E_INVALID;
+    }
+    rba::PrologueParams p{};
+    p.B = a->B, p.T = a->T, p.Hq = a->Hq, p.Hkv = a->Hkv, p.W = a->conv_w, p.Skv = c->Skv;
+    p.eps = a->eps;
+    p.cu_new = a->cu_new, p.seq_lens = a->seq_lens;
+    p.q = (const __bf16 *)a->q, p.k = (const __bf16 *)a->k, p.v = (const __bf16 *)a->v;
+    p.qs0 = a->q_s[0], p.qs1 = a->q_s[1], p.ks0 = a->k_s[0], p.ks1 = a->k_s[1];
+    p.vs0 = a->v_s[0], p.vs1 = a->v_s[1], p.qos0 = a->q_out_s[0], p.qos1 = a->q_out_s[1];
+    p.conv_wk = a->conv_wk, p.conv_wv = a->conv_wv, p.norm_q = a->norm_q, p.norm_k = a->norm_k;
+    p.state_k = (__bf16 *)a->state_k, p.state_v = (__bf16 *)a->state_v, p.q_out = (__bf16 *)a->q_out;
+    p.k_cache = const_cast<void *>(c->k), p.v_cache = const_cast<void *>(c->v);
+    p.cks0 = c->k_s[0], p.cks1 = c->k_s[1], p.cks2 = c->k_s[2];
+    p.cvs0 = c->v_s[0], p.cvs1 = c->v_s[1], p.cvs2 = c->v_s[2];
+    if (f8) {
+        p.k_scale = (uint8_t *)const_cast<void *>(c->k_scale);
+        p.v_scale = (uint8_t *)const_cast<void *>(c->v_scale);
+        p.sks0 = c->k_scale_s[0], p.sks1 = c->k_scale_s[1], p.sks2 = c->k_scale_s[2];
+        p.svs0 = c->v_scale_s[0], p.svs1 = c->v_scale_s[1], p.svs2 = c->v_scale_s[2];
+    }
+    if (kv != nullptr) {
+        p.block_table = kv->block_table, p.bt_stride = kv->bt_stride;
+        p.page_size = kv->page_size, p.num_pages = kv->num_pages;
+    }
+    return rba::launch_prologue(p, (hipStream_t)stream) == hipSuccess ? RBA_OK : RBA_E_LAUNCH;
 }
 
 rba_status rba_splitkv_combine(const float *o_part, const float *lse_part, int num_splits,

@@ -42,6 +42,27 @@ struct AttnParams {
     int64_t kss0, kss1, kss2, vss0, vss1, vss2;
 };
 
+// One attention-prologue launch (ShortConv, RMSNorm, cache write) for T new
+// tokens of B sequences; bf16 projections, fp32 weights.
+struct PrologueParams {
+    int B, T, Hq, Hkv, W, Skv;
+    float eps;
+    const int *cu_new, *seq_lens;
+    const __bf16 *q, *k, *v;
+    int64_t qs0, qs1, ks0, ks1, vs0, vs1, qos0, qos1;
+    const float *conv_wk, *conv_wv, *norm_q, *norm_k;
+    __bf16 *state_k, *state_v, *q_out;
+    void *k_cache, *v_cache;                   // bf16, or MXFP8 codes when k_scale != null
+    int64_t cks0, cks1, cks2, cvs0, cvs1, cvs2;
+    uint8_t *k_scale, *v_scale;
+    int64_t sks0, sks1, sks2, svs0, svs1, svs2;
+    const int *block_table;                    // paged cache when != null
+    int64_t bt_stride;
+    int page_size, num_pages;
+};
+
+hipError_t launch_prologue(const PrologueParams &p, hipStream_t stream);
+
 // Kernel variants.  WIDE: two 32-column tiles per wave (prefill, bf16).
 enum class AttnVariant { BF16_WIDE, BF16_NARROW, FP32 };
 

@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("rba_relproj", "rba_attn_prefill", "rba_attn_decode", "rba_attn_paged", "rba_splitkv_combine",
-                 "rba_mxfp8_quantize",
+                 "rba_mxfp8_quantize", "rba_attn_prologue",
                  "rba_num_splits", "rba_decode_workspace_bytes", "rba_status_string"):
         assert must in names
 
@@ -221,6 +221,82 @@ def test_mxfp8_quantize_validation():
     assert f(1, 4, 128, px, 128, pc, 128, ps, 3, None) == RBA_E_INVALID
     assert f(1, 4, 128, px, 128, pc, 128, None, 4, None) == RBA_E_INVALID
     assert f(5, 4, 128, px, 128, pc, 128, ps, 4, None) == RBA_E_UNSUPPORTED
+
+
+def _prologue_abi(T=3, B=2, Hq=4, Hkv=2, W=4, f8=False):
+    q = torch.zeros(T, Hq, 128, dtype=torch.bfloat16)
+    k = torch.zeros(T, Hkv, 128, dtype=torch.bfloat16)
+    v = torch.zeros_like(k)
+    cu = torch.tensor([0, 1, T], dtype=torch.int32)
+    lens = torch.tensor([5, 9], dtype=torch.int32)
+    wk = torch.zeros(Hkv * 128, W)
+    nq = torch.ones(128)
+    st = torch.zeros(B, W - 1, Hkv, 128, dtype=torch.bfloat16)
+    qo = torch.zeros_like(q)
+    kc = torch.zeros(B, 16, Hkv, 128, dtype=torch.uint8 if f8 else torch.bfloat16)
+    sc = torch.zeros(B, 16, Hkv, 4, dtype=torch.uint8) if f8 else None
+    keep = (q, k, v, cu, lens, wk, nq, st, qo, kc, sc)
+    a = rba._PrologueArgs()
+    a.B, a.T, a.Hq, a.Hkv, a.d, a.conv_w, a.eps = B, T, Hq, Hkv, 128, W, 1e-6
+    a.cu_new, a.seq_lens, a.q, a.k, a.v = cu.data_ptr(), lens.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.q_s[:] = [q.stride(0), q.stride(1)]
+    a.k_s[:] = [k.stride(0), k.stride(1)]
+    a.v_s[:] = [v.stride(0), v.stride(1)]
+    a.conv_wk = a.conv_wv = wk.data_ptr()
+    a.norm_q = a.norm_k = nq.data_ptr()
+    a.state_k = a.state_v = st.data_ptr()
+    a.q_out = qo.data_ptr()
+    a.q_out_s[:] = [qo.stride(0), qo.stride(1)]
+    c = rba.cache_args(kc, kc, k_scale=sc, v_scale=sc)
+    return a, c, keep
+
+
+def _prologue_call(a, c, kv=None):
+    return lib.rba_attn_prologue(ctypes.byref(a), None if c is None else ctypes.byref(c),
+                                 None if kv is None else ctypes.byref(kv), None)
+
+
+def test_prologue_validation():
+    cases = [
+        (lambda a, c: setattr(a, "d", 64), RBA_E_UNSUPPORTED),
+        (lambda a, c: setattr(a, "d", 0), RBA_E_INVALID),
+        (lambda a, c: setattr(a, "conv_w", 0), RBA_E_INVALID),
+        (lambda a, c: setattr(a, "conv_w", 9), RBA_E_INVALID),
+        (lambda a, c: setattr(a, "eps", 0.0), RBA_E_INVALID),
+        (lambda a, c: setattr(a, "eps", float("inf")), RBA_E_INVALID),
+        (lambda a, c: setattr(a, "Hkv", 3), RBA_E_INVALID),
+        (lambda a, c: setattr(a, "B", 0), RBA_E_INVALID),
+        (lambda a, c: setattr(a, "cu_new", None), RBA_E_INVALID),
+        (lambda a, c: setattr(a, "state_k", None), RBA_E_INVALID),
+        (lambda a, c: setattr(a, "q", a.q + 2), RBA_E_INVALID),
+        (lambda a, c: a.k_s.__setitem__(0, 258), RBA_E_INVALID),
+        (lambda a, c: setattr(c, "dt", 0), RBA_E_UNSUPPORTED),
+        (lambda a, c: setattr(c, "kv_format", 3), RBA_E_INVALID),
+        (lambda a, c: setattr(c, "Skv", 0), RBA_E_INVALID),
+        (lambda a, c: c.v_s.__setitem__(1, 6), RBA_E_INVALID),
+    ]
+    for mutate, want in cases:
+        a, c, keep = _prologue_abi()
+        mutate(a, c)
+        assert _prologue_call(a, c) == want
+    a, c, keep = _prologue_abi()
+    assert _prologue_call(a, None) == RBA_E_INVALID
+    a, c, keep = _prologue_abi(f8=True)
+    c.k_scale = None
+    assert _prologue_call(a, c) == RBA_E_INVALID
+    # paged destination: page size and table checked like the attention's
+    a, c, keep = _prologue_abi()
+    table = torch.zeros(2, 1, dtype=torch.int32)
+    kv = rba.make_paged(table, keep[4], 32, 4)
+    assert _prologue_call(a, c, kv) == RBA_E_INVALID
+    kv = rba.make_paged(table, keep[4], 64, 4)
+    c.Skv = 65                                  # two pages needed, one table column
+    assert _prologue_call(a, c, kv) == RBA_E_INVALID
+    # nothing to do
+    a, c, keep = _prologue_abi()
+    a.T = 0
+    a.q = a.k = a.v = a.q_out = None
+    assert _prologue_call(a, c) == RBA_OK
 
 
 def test_calib_validation():

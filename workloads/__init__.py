@@ -6,6 +6,6 @@ method is computed here.  Both the fp64 oracle (``oracle/``) and the HIP path
 sides see the same values without sharing any arithmetic.
 """
 from .configs import CONFIGS, Workload, get
-from .gen import make_inputs, make_paged_inputs, randn
+from .gen import make_inputs, make_paged_inputs, make_prologue_inputs, randn
 
-__all__ = ["CONFIGS", "Workload", "get", "make_inputs", "make_paged_inputs", "randn"]
+__all__ = ["CONFIGS", "Workload", "get", "make_inputs", "make_paged_inputs", "make_prologue_inputs", "randn"]

@@ -70,3 +70,39 @@ def make_paged_inputs(w: Workload, page_size: int, seq_lens=None, seed: int | No
     out["block_table"] = table
     out["seq_lens"] = lens.to(torch.int32)
     return out
+
+
+def make_prologue_inputs(new_tokens, seq_lens, Hq=64, Hkv=8, d=128, W=4, seed=2001) -> dict:
+    """CPU tensors for one attention-prologue call: B sequences receiving
+    new_tokens[b] tokens, ending at lengths seq_lens[b].
+
+      q, k, v      : bf16 [T, Hq|Hkv, d] ~ N(0, 1) (projections)
+      conv_wk/wv   : fp32 [Hkv*d, W] ~ N(0, 1/W) (taps)
+      norm_q/k     : fp32 [d] ~ 1 + N(0, 0.1) (RMSNorm weights)
+      state_k/v    : bf16 [B, W-1, Hkv, d] ~ N(0, 1), zero for positions
+                     before a sequence's start
+      cu_new       : int32 [B+1], seq_lens int32 [B]
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    T = int(sum(new_tokens))
+    B = len(new_tokens)
+    q = randn((T, Hq, d), g).to(torch.bfloat16)
+    k = randn((T, Hkv, d), g).to(torch.bfloat16)
+    v = randn((T, Hkv, d), g).to(torch.bfloat16)
+    wk = randn((Hkv * d, W), g, (1.0 / W) ** 0.5)
+    wv = randn((Hkv * d, W), g, (1.0 / W) ** 0.5)
+    nq = 1.0 + randn((d,), g, 0.1)
+    nk = 1.0 + randn((d,), g, 0.1)
+    sk = randn((B, max(W - 1, 0), Hkv, d), g).to(torch.bfloat16)
+    sv = randn((B, max(W - 1, 0), Hkv, d), g).to(torch.bfloat16)
+    for b in range(B):
+        start = int(seq_lens[b]) - int(new_tokens[b])
+        for j in range(W - 1):
+            if start - (W - 1) + j < 0:
+                sk[b, j] = 0
+                sv[b, j] = 0
+    cu = torch.zeros(B + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.as_tensor(new_tokens, dtype=torch.int64), 0).to(torch.int32)
+    return {"q": q, "k": k, "v": v, "conv_wk": wk, "conv_wv": wv, "norm_q": nq, "norm_k": nk,
+            "state_k": sk, "state_v": sv, "cu_new": cu, "seq_lens": torch.as_tensor(seq_lens, dtype=torch.int32)}
