@@ -239,6 +239,50 @@ def paged_decode_leg(rba, torch, name, page_size, reps, len_lo, seed=77):
     return res
 
 
+def prologue_leg(rba, torch, name, new_tokens, seq_lens, Skv, reps, mxfp8=False):
+    """The attention prologue (K/V ShortConv W=4, Q/K RMSNorm, cache write) for a
+    batch of new tokens with 64 query / 8 kv heads; HBM-bound."""
+    from workloads import make_prologue_inputs
+    inp = make_prologue_inputs(new_tokens, seq_lens, Hq=64, Hkv=8, W=4)
+    d = {k: v.to("cuda") for k, v in inp.items()}
+    B, T = len(new_tokens), int(sum(new_tokens))
+    if mxfp8:
+        kc = torch.zeros(B, Skv, 8, 128, dtype=torch.uint8, device="cuda")
+        vc = torch.zeros_like(kc)
+        ks = torch.zeros(B, Skv, 8, 4, dtype=torch.uint8, device="cuda")
+        vs = torch.zeros_like(ks)
+    else:
+        kc = torch.zeros(B, Skv, 8, 128, dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        ks = vs = None
+    qo = torch.empty_like(d["q"])
+    # the call once through the binding (checks), then the C entry point with prebuilt arguments
+    rba.attn_prologue(d["q"], d["k"], d["v"], d["cu_new"], d["seq_lens"], d["conv_wk"], d["conv_wv"], d["norm_q"],
+                      d["norm_k"], d["state_k"], d["state_v"], kc, vc, k_scale=ks, v_scale=vs, q_out=qo)
+    a = rba._PrologueArgs()
+    a.B, a.T, a.Hq, a.Hkv, a.d, a.conv_w, a.eps = B, T, 64, 8, 128, 4, 1e-6
+    a.cu_new, a.seq_lens = d["cu_new"].data_ptr(), d["seq_lens"].data_ptr()
+    a.q, a.k, a.v = d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr()
+    for nm, t in (("q_s", d["q"]), ("k_s", d["k"]), ("v_s", d["v"]), ("q_out_s", qo)):
+        getattr(a, nm)[:] = [t.stride(0), t.stride(1)]
+    a.conv_wk, a.conv_wv = d["conv_wk"].data_ptr(), d["conv_wv"].data_ptr()
+    a.norm_q, a.norm_k = d["norm_q"].data_ptr(), d["norm_k"].data_ptr()
+    a.state_k, a.state_v, a.q_out = d["state_k"].data_ptr(), d["state_v"].data_ptr(), qo.data_ptr()
+    c = rba.cache_args(kc, vc, k_scale=ks, v_scale=vs)
+    launch = c_launcher(rba, "rba_attn_prologue", ctypes.byref(a), ctypes.byref(c), None, rba._stream(qo.device))
+    ms = time_launches(launch, reps, torch)
+    row = 128 * 2
+    kv_row = 132 if mxfp8 else row
+    # q, k, v read once; conv-state rows read and written; q_out and the cache rows written
+    nbytes = T * (64 + 16) * row + 2 * B * 3 * 8 * row * 2 + T * 64 * row + T * 16 * kv_row
+    res = {"ms": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": nbytes, "tokens": T,
+           "cache": "MXFP8" if mxfp8 else "bf16", "timing": "back-to-back mean after a clock warm-up"}
+    del d, kc, vc, ks, vs, qo
+    torch.cuda.empty_cache()
+    return res
+
+
 def attainable(rba, torch):
     """Streaming-read bandwidth and bf16 MFMA rate this device attains (the library's
     measurement aids, timed like the kernels)."""
@@ -366,6 +410,12 @@ def main():
         out["decode"]["c4_decode_full_paged64"] = paged_decode_leg(rba, torch, "c4_decode_full", 64, 20, 8192)
         for name in ("c4_decode_full", "c5_long_decode"):
             out["decode"][name + "_mxfp8"] = decode_leg(rba, torch, name, 20, mxfp8=True)
+    log("attention prologue ...")
+    out["prologue"] = {
+        "prefill_8192": prologue_leg(rba, torch, "prefill", [8192], [8192], 8192, 20),
+        "decode_64x9": prologue_leg(rba, torch, "decode", [9] * 64, [9216] * 64, 9216, 50),
+        "decode_64x9_mxfp8": prologue_leg(rba, torch, "decode", [9] * 64, [9216] * 64, 9216, 50, mxfp8=True),
+    }
     att = attainable(rba, torch)
     out["attainable"] = att
     out["roofline"]["frac_attainable"] = round(out["roofline"]["achieved"] / att["mfma_bf16_TFLOPs"], 4)
