@@ -283,6 +283,34 @@ def prologue_leg(rba, torch, name, new_tokens, seq_lens, Skv, reps, mxfp8=False)
     return res
 
 
+def full_prefill_leg(rba, torch, reps=5):
+    """Full-causal prefill with the length-dependent log scale (B=2, S=32768, 64/8
+    heads, E=512): relproj + attention, and the attention kernel alone."""
+    from workloads import CONFIGS, make_inputs
+    w = CONFIGS["c3_full_prefill"]
+    log("full prefill: generating inputs")
+    inp = make_inputs(w)
+    d = {k: v.to("cuda") for k, v in inp.items()}
+    del inp
+    R = rba.relproj(d["r"], d["P"])
+    o = torch.empty_like(d["q"])
+    a = rba.make_args(d["q"], d["k"], d["v"], R, o, None, window=w.window, log_scale_base=w.log_scale_base)
+    ms = time_launches(c_launcher(rba, "rba_attn_prefill", ctypes.byref(a), rba._stream(o.device)), reps, torch)
+    r2 = d["r"].reshape(-1, w.r_dim)
+    ms_rp = time_launches(c_launcher(rba, "rba_relproj", 1, 1, r2.shape[0], w.Hq, w.r_dim, w.E,
+                                     ctypes.c_void_p(r2.data_ptr()), r2.stride(0), 0,
+                                     ctypes.c_void_p(d["P"].data_ptr()), ctypes.c_void_p(R.data_ptr()),
+                                     rba._stream(o.device)), reps, torch)
+    flops = w.attn_flops()
+    res = {"attn_ms": round(ms, 3), "attn_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "relproj_ms": round(ms_rp, 3), "step_tflops": round(flops / ((ms + ms_rp) * 1e-3) / 1e12, 1),
+           "algorithmic_flops": flops, "timing": "back-to-back mean after a clock warm-up"}
+    del d, R, o
+    torch.cuda.empty_cache()
+    return res
+
+
 def attainable(rba, torch):
     """Streaming-read bandwidth and bf16 MFMA rate this device attains (the library's
     measurement aids, timed like the kernels)."""
@@ -410,6 +438,8 @@ def main():
         out["decode"]["c4_decode_full_paged64"] = paged_decode_leg(rba, torch, "c4_decode_full", 64, 20, 8192)
         for name in ("c4_decode_full", "c5_long_decode"):
             out["decode"][name + "_mxfp8"] = decode_leg(rba, torch, name, 20, mxfp8=True)
+    if not args.no_decode:
+        out["prefill_full_causal"] = full_prefill_leg(rba, torch)
     log("attention prologue ...")
     out["prologue"] = {
         "prefill_8192": prologue_leg(rba, torch, "prefill", [8192], [8192], 8192, 20),
