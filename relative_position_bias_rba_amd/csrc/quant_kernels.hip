@@ -8,11 +8,11 @@
 // Attention と FA4 経路") and name FP8 as the way to relieve the KV cache
 // ("vLLM TML Inkling サポート").
 //
-// Eight lanes encode one block (4 entries each): the block maximum is
-// exchanged among them, each lane scales its entries exactly (ldexp), clamps
-// them to +-448 and converts them with the hardware's round-to-nearest-even
-// E4M3 conversion, then writes one dword of codes; the block's first lane
-// writes the scale byte.  Bound by HBM (2 or 4 bytes read, 1.03 written per
+// Four lanes encode one block (8 entries each, one 16-byte load of bf16):
+// the block maximum is exchanged among them, each lane scales its entries
+// exactly (ldexp), clamps them to +-448 and converts them with the
+// hardware's round-to-nearest-even E4M3 conversion, then writes two dwords
+// of codes; the block's first lane writes the scale byte.  Bound by HBM (2 or 4 bytes read, 1.03 written per
 // entry).
 #include "rba_internal.h"
 
@@ -22,6 +22,7 @@ namespace rba {
 namespace {
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <typename TI>
@@ -29,38 +30,46 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const TI *__restric
                                                             int64_t xs, uint8_t *__restrict__ q, int64_t qs,
                                                             uint8_t *__restrict__ sc, int64_t ss) {
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t blk = g >> 3;            // the 8 lanes of a block are adjacent and share validity
-    const int sub = (int)(g & 7);
+    const int64_t blk = g >> 2;            // the 4 lanes of a block are adjacent and share validity
+    const int sub = (int)(g & 3);
     const int64_t row = blk / nblk;
     if (row >= rows) return;
     const int bi = (int)(blk - row * nblk);
-    const int e0 = 32 * bi + 4 * sub;
-    float v[4];
+    const int e0 = 32 * bi + 8 * sub;
+    float v[8];
     if constexpr (sizeof(TI) == 2) {
-        const u32x2 w = *(const u32x2 *)(x + row * xs + e0);
+        const u32x4 w = *(const u32x4 *)(x + row * xs + e0);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 4; ++i) {
             v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
             v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
         }
     } else {
-        const f32x4 w = *(const f32x4 *)(x + row * xs + e0);
+        const f32x4 w0 = *(const f32x4 *)(x + row * xs + e0), w1 = *(const f32x4 *)(x + row * xs + e0 + 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = w[i];
+        for (int i = 0; i < 4; ++i) {
+            v[i] = w0[i];
+            v[4 + i] = w1[i];
+        }
     }
-    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     amax = fmaxf(amax, __shfl_xor(amax, 2));
-    amax = fmaxf(amax, __shfl_xor(amax, 4));
     // floor(log2 amax) = frexp exponent - 1 (exact, subnormals included)
     int e = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 1 - 8 : -127;
     e = min(max(e, -127), 127);
-    float s[4];
+    float s[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = fminf(fmaxf(ldexpf(v[i], -e), -448.f), 448.f);
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[0], s[1], 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(s[2], s[3], w, true);
-    *(unsigned *)(q + row * qs + e0) = (unsigned)w;
+    for (int i = 0; i < 8; ++i) s[i] = fminf(fmaxf(ldexpf(v[i], -e), -448.f), 448.f);
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(s[0], s[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(s[2], s[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(s[4], s[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(s[6], s[7], w1, true);
+    unsigned *dst = (unsigned *)(q + row * qs + e0);
+    dst[0] = (unsigned)w0;
+    dst[1] = (unsigned)w1;
     if (sub == 0) sc[row * ss + bi] = (uint8_t)(e + 127);
 }
 
@@ -69,7 +78,7 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const TI *__restric
 hipError_t launch_mxfp8_quantize(bool in_bf16, int64_t rows, int n, const void *x, int64_t x_stride, void *codes,
                                  int64_t codes_stride, void *scales, int64_t scales_stride, hipStream_t stream) {
     const int nblk = n / 32;
-    const int64_t lanes = rows * nblk * 8;
+    const int64_t lanes = rows * nblk * 4;
     const int64_t grid = (lanes + 255) / 256;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (in_bf16)
