@@ -89,7 +89,7 @@ def _load():
     if not os.path.exists(lib_path):
         raise ImportError(
             f"librba.so not found at {lib_path}; build it with "
-            "`python -m relative_position_bias_rba_amd.build` (hipcc, gfx950)")
+            "`python relative_position_bias_rba_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(lib_path)
     P = ctypes.POINTER(_AttnArgs)
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int

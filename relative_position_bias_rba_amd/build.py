@@ -1,6 +1,6 @@
 """Build librba.so (the C-ABI library with the gfx950 kernels) in-tree.
 
-    python -m relative_position_bias_rba_amd.build
+    python relative_position_bias_rba_amd/build.py
 
 compiles csrc/*.hip and csrc/*.cpp with hipcc for gfx950 into
 relative_position_bias_rba_amd/librba.so.  Packed fp32 instructions are
