@@ -398,6 +398,6 @@ const char *rba_status_string(rba_status status) {
     return "unknown status";
 }
 
-int rba_version(void) { return 100; }
+int rba_version(void) { return 200; }
 
 }  // extern "C"

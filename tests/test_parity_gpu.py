@@ -104,6 +104,43 @@ def test_relproj_per_head_parity(T, Hq, r_dim, E, dt, sliced):
         assert np.all(np.abs(g_ - want) <= 2.0 ** -8 * np.abs(want) + 1e-6)
 
 
+@pytest.mark.parametrize("case", ["wide_g256", "decode_g256", "narrow_g128", "fp32_g128", "mxfp8_g128"])
+def test_largest_groups(case):
+    """The largest query-head groups each variant takes (one query row per block)."""
+    m = rba()
+    cfg = {
+        "wide_g256": ("c2_swa_prefill", dict(B=1, Sq=40, Skv=100, Hq=256, Hkv=1, E=32, window=0), None),
+        "decode_g256": ("c4_decode_full", dict(B=2, Sq=1, Skv=300, Hq=256, Hkv=1, E=32, window=0), 3),
+        "narrow_g128": ("c4_decode_full", dict(B=2, Sq=1, Skv=300, Hq=128, Hkv=1, E=32, window=64), 2),
+        "fp32_g128": ("c1_tiny_fp32", dict(B=1, Sq=5, Skv=70, Hq=128, Hkv=1, E=16), None),
+        "mxfp8_g128": ("c4_decode_full", dict(B=2, Sq=1, Skv=300, Hq=128, Hkv=1, E=32, window=0), 3),
+    }[case]
+    w = small(CONFIGS[cfg[0]], **cfg[1])
+    say(f"largest group {case}: {w}")
+    inp = make_inputs(w)
+    d = to_dev(inp)
+    R = m.relproj(d["r"], d["P"])
+    kw = dict(window=w.window, log_scale_base=w.log_scale_base, return_lse=True)
+    k, v = inp["k"], inp["v"]
+    if case == "mxfp8_g128":
+        kc, ks = oracle.mxfp8_quantize(inp["k"])
+        vc, vs = oracle.mxfp8_quantize(inp["v"])
+        k, v = oracle.mxfp8_dequantize(kc, ks), oracle.mxfp8_dequantize(vc, vs)
+        o, lse = m.attn_decode(d["q"], torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV), R,
+                               num_splits=cfg[2], k_scale=torch.from_numpy(ks).to(DEV),
+                               v_scale=torch.from_numpy(vs).to(DEV), **kw)
+    elif cfg[2] is None:
+        o, lse = m.attn_prefill(d["q"], d["k"], d["v"], R, **kw)
+    else:
+        o, lse = m.attn_decode(d["q"], d["k"], d["v"], R, num_splits=cfg[2], **kw)
+    torch.cuda.synchronize()
+    wo, wl = oracle.attention(inp["q"], k, v, oracle.relproj(inp["r"], inp["P"]), window=w.window,
+                              log_scale_base=w.log_scale_base)
+    fp32 = w.dtype == "fp32"
+    check(f"{case} o", o, wo, fp32)
+    check(f"{case} lse", lse, wl, True, extra_tol=None if fp32 else 2e-2)
+
+
 def test_calibration_kernels_run():
     """The measurement aids launch, report their flop count and leave the sink alone."""
     import ctypes
