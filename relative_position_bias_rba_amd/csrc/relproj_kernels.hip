@@ -35,7 +35,7 @@ constexpr int TT = 1;         // 32-token column tiles per wave
 constexpr int TPW = 32 * TT;  // tokens per wave
 constexpr int TPB = 4 * TPW;  // tokens per workgroup
 constexpr int KMAX = 128;     // largest r_dim
-constexpr int kMaxTokenBlocks = 8;
+constexpr int kMaxTokenBlocks = 4;
 constexpr int kMinWorkgroups = 4096;
 
 __device__ __forceinline__ int mfma_row_key(int i) { return ((i >> 2) & 1) * 16 + (i >> 3) * 4 + (i & 3); }
