@@ -933,16 +933,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     const bool wave_active = wave * 32 < ncols;
     const int rb = (prow - N + 1) & ~(CH - 1);
 
-    bf16x8 qf[8];
-    {
-        const T *qp = (const T *)p.q + (int64_t)b * p.qs0 + (int64_t)tq * p.qs1 + (int64_t)hq * p.qs2;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) qf[k] = cvalid ? *(const bf16x8 *)(qp + 16 * k + 8 * hh) : bf16x8{};
-        // Settle the loads here: otherwise the compiler's wait for them sits
-        // inside the phase loop, where it would also wait for the DMA.
-#pragma unroll
-        for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(qf[k]));
-    }
+    bf16x8 qf[8];                 // loaded after the first tile's staging is issued
 
     f32x16 O[4];
     f32x16 S[KT];
@@ -1239,9 +1230,20 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
             }
 #pragma unroll
             for (int s = 0; s < NKI + NVI + NSI; ++s) issue(s);
-            wait_vmem();
         }
     }
+    // Q fragments, in flight together with the first tile's staging.  Settle
+    // them here: otherwise the compiler's wait for them sits inside the phase
+    // loop, where it would also wait for the DMA.  vmcnt counts in order, so
+    // the wait for Q also lands the staging.
+    {
+        const T *qp = (const T *)p.q + (int64_t)b * p.qs0 + (int64_t)tq * p.qs1 + (int64_t)hq * p.qs2;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) qf[k] = cvalid ? *(const bf16x8 *)(qp + 16 * k + 8 * hh) : bf16x8{};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(qf[k]));
+    }
+    wait_vmem();
     lds_barrier();
 
     // ------------------------------------------------------------ phases 2t, 2t+1 for t = 0..n_it
