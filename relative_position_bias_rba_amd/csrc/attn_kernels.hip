@@ -37,6 +37,7 @@
 
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 namespace rba {
@@ -855,7 +856,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 // (16-byte chunks XOR-swizzled by row) and read as the PV A-operand with the
 // LDS transpose read, so it never passes through registers.  LDS regions are
 // padded to whole DMA instructions so no lane needs masking.
-__global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParams p) {
+__global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParams p_arg) {
+    typedef const __attribute__((address_space(4))) AttnParams CParams;
     typedef __bf16 T;
     typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
     constexpr int ES = 2;
@@ -882,19 +884,47 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     __shared__ __attribute__((aligned(16))) T sV[2][N * D];
     __shared__ __attribute__((aligned(16))) T sR[2][2][NSI * GT * CH];   // [group][buffer]
 
-    const int tid = threadIdx.x;
+    // ------------------------------------------------------------ work item
+    const int per_bh = p_arg.nqb * p_arg.splits;
+    const int total = p_arg.B * p_arg.Hkv * per_bh;
+    // The grid may be smaller than the item count (one workgroup per CU);
+    // each workgroup then takes its items round by round.  With grid and
+    // item counts multiples of 8 (workgroup w runs on XCD w mod 8), XCD x
+    // owns the x-th eighth of the items, longest first, and its workgroups
+    // take them in snake order (forward in even rounds, backward in odd
+    // ones) so that long and short blocks pair up.
+    const bool xcd_map = (total & 7) == 0 && (gridDim.x & 7) == 0;
+    const int n8 = total >> 3, nx = gridDim.x >> 3, jx = blockIdx.x >> 3, x8 = blockIdx.x & 7;
+    const int n_rounds = xcd_map ? (n8 + nx - 1) / nx : (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    for (int rnd = 0; rnd < n_rounds; ++rnd) {
+    // The parameters are read afresh in every round (from the constant
+    // kernel-argument segment, scalar loads) rather than held in registers
+    // across rounds.
+#if __HIP_DEVICE_COMPILE__
+    CParams *pk = (CParams *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(pk));
+    const AttnParams p = *pk;
+#else
+    const AttnParams p = p_arg;
+#endif
+    // Likewise the lane's own indices, so that nothing derived from them is
+    // hoisted out of the round loop and held (or spilled) across it.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int grp = wave >> 2;
     const int gw = wave & 3;
     const int hh = lane >> 5;
     const int lc = lane & 31;
-
-    // ------------------------------------------------------------ work item
-    const int per_bh = p.nqb * p.splits;
-    const int total = p.B * p.Hkv * per_bh;
-    int item = blockIdx.x;
-    if ((total & 7) == 0) item = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    int item;
+    if (xcd_map) {
+        const int k = rnd * nx + ((rnd & 1) ? nx - 1 - jx : jx);
+        if (k >= n8) continue;
+        item = x8 * n8 + k;
+    } else {
+        item = blockIdx.x + rnd * gridDim.x;
+    }
     const int bh = item / per_bh;
     const int rem = item - bh * per_bh;
     const int qb = p.nqb - 1 - rem / p.splits;
@@ -1290,7 +1320,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
 
     // ------------------------------------------------------------ epilogue
     const float lt = l + __shfl_xor(l, 32);
-    if (!cvalid) return;
+    if (cvalid) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse_v = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
     if (p.splits == 1) {
@@ -1319,6 +1349,8 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
             }
         if (hh == 0) p.lse_part[row] = lse_v;
     }
+    }  // cvalid
+    }  // work items
 }
 
 // Split-KV merge.  32 lanes cover one output row (4 head-dim entries each);
@@ -1394,6 +1426,23 @@ __global__ __launch_bounds__(NT) void combine_kernel(const float *__restrict__ o
 
 }  // namespace
 
+// Grid of the persistent prefill kernel: one workgroup per CU (a multiple
+// of 8, so the XCD-aware item order holds) when the items outnumber the CUs
+// and split evenly over the 8 XCDs; else one workgroup per item.
+static int pp_grid(int64_t items) {
+    static std::atomic<int> cus_of[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return (int)items;
+    int cus = cus_of[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return (int)items;
+        cus_of[dev].store(cus, std::memory_order_relaxed);
+    }
+    const int g = cus & ~7;
+    return (items % 8 == 0 && g >= 8 && items > g) ? g : (int)items;
+}
+
 int attn_max_columns(AttnVariant v) { return v == AttnVariant::BF16_WIDE ? 256 : 128; }
 
 hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stream) {
@@ -1414,8 +1463,8 @@ hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stre
                 RBA_FWD(__bf16, 8, true, false, true);
             else if (paged)
                 RBA_FWD(__bf16, 8, true, true, false);
-            else if (p.kv32)            // two ping-pong groups
-                hipLaunchKernelGGL(attn_prefill_pp_kernel, grid, dim3(512), 0, stream, p);
+            else if (p.kv32)            // two ping-pong groups, one workgroup per CU
+                hipLaunchKernelGGL(attn_prefill_pp_kernel, dim3(pp_grid(blocks)), dim3(512), 0, stream, p);
             else
                 RBA_FWD(__bf16, 8, true, false, false);
             break;
