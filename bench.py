@@ -311,6 +311,29 @@ def full_prefill_leg(rba, torch, reps=5):
     return res
 
 
+def fused_prefill_leg(rba, torch, w, d, reps, two_kernel_ms):
+    """rba_attn_prefill_fused on the same workload: relproj and attention in one
+    launch, the rows of R kept in a per-workgroup workspace instead of HBM."""
+    dev = d["q"].device
+    PT = rba.relproj_pack(d["P"])
+    o = torch.empty_like(d["q"])
+    a = rba.make_args(d["q"], d["k"], d["v"], None, o, None, window=w.window, log_scale_base=w.log_scale_base)
+    a.E = w.E
+    rb = rba.make_relbias(d["r"], PT)
+    need = rba._lib.rba_prefill_fused_workspace_bytes(ctypes.byref(a))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ms = time_launches(c_launcher(rba, "rba_attn_prefill_fused", ctypes.byref(a), ctypes.byref(rb),
+                                  ctypes.c_void_p(ws.data_ptr()), need, rba._stream(dev)), reps, torch)
+    flops = w.attn_flops()
+    res = {"ms": round(ms, 4), "step_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "two_kernel_ms": round(two_kernel_ms, 4), "speedup_vs_two_kernels": round(two_kernel_ms / ms, 4),
+           "workspace_bytes": need, "kernel": "attn_prefill_pp_kernel<4> (relative logits computed in place)",
+           "timing": "back-to-back mean after a clock warm-up"}
+    del ws, o, PT
+    return res
+
+
 def attainable(rba, torch):
     """Streaming-read bandwidth and bf16 MFMA rate this device attains (the library's
     measurement aids, timed like the kernels)."""
@@ -426,6 +449,7 @@ def main():
                     "relproj_GBps": round(relproj_bytes / (ms_relproj * 1e-3) / 1e9, 1),
                     "relproj_frac_hbm": round(relproj_bytes / (ms_relproj * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
     }
+    out["prefill_fused"] = fused_prefill_leg(rba, torch, w, d, max(args.steps, 10), ms_attn + ms_relproj)
     del R, o
     d_cpu = inp
     del d

@@ -135,6 +135,54 @@ rba_status rba_relproj(rba_dtype in_dt, rba_dtype out_dt, int64_t T, int Hq, int
  * Sq = 0 is a no-op.                                                         */
 rba_status rba_attn_prefill(const rba_attn_args *args, void *stream);
 
+/* The projection weights repacked for rba_attn_prefill_fused ([S-RPB]):
+ * P [Hq, r_dim, E] bf16, contiguous, 16-byte aligned, is rewritten into PT,
+ * rba_relproj_packed_bytes(Hq, r_dim, E) bytes (16-byte aligned), in the
+ * order the fused kernel's matrix-core operands read it: for head h, tile
+ * eb of 32 distances, k-step k of 16 channels and lane l of a 64-lane wave,
+ * the 8 values P[h, 16k + 8(l/32) + x, 32 eb + m(l % 32)], x = 0..7, are
+ * consecutive, with m(i) = 16((i/4) % 2) + 4(i/8) + i % 4; entries past E are
+ * zero.  The layout is otherwise opaque.  r_dim a multiple of 16, at most 128
+ * (else RBA_E_UNSUPPORTED).  A weight is packed once and reused.            */
+size_t rba_relproj_packed_bytes(int Hq, int r_dim, int E);
+rba_status rba_relproj_pack(int Hq, int r_dim, int E, const void *P, void *PT, void *stream);
+
+/* Relative-feature operands of rba_attn_prefill_fused ([S-RPB]):
+ *   r   : [B, Sq, r_dim] shared by the heads (r_s[2] = 0) or [B, Sq, Hq,
+ *         r_dim] one feature per head; strides r_s = {b, t, h} in elements,
+ *         channel contiguous, multiples of 8; bf16, 16-byte aligned
+ *   PT  : the projection as packed by rba_relproj_pack, 16-byte aligned
+ *   r_dim : a multiple of 16, 16 <= r_dim <= 128                            */
+typedef struct rba_relbias {
+    int r_dim;
+    const void *r;
+    int64_t r_s[3];
+    const void *PT;
+} rba_relbias;
+
+/* Bytes of workspace rba_attn_prefill_fused needs for `args` on the current
+ * device: one region of QB * (Hq/Hkv) * 32 ceil(E/32) bf16 entries per
+ * workgroup (QB = query rows per block, at most 32), where a workgroup keeps
+ * the rows of R of the query block it is working on.
+ * 0 if the call is invalid or unsupported.                                  */
+size_t rba_prefill_fused_workspace_bytes(const rba_attn_args *args);
+
+/* rba_relproj and rba_attn_prefill in one launch ([S-RPB]): the same outputs,
+ * bit for bit, as rba_relproj (bf16 out) into an R that rba_attn_prefill then
+ * reads, but each workgroup computes the rows of R its query block needs
+ * (all E distances of its rows, on MFMA) into its region of `workspace` and
+ * reads them from there, so R never makes the round trip through HBM.
+ * args->R must be NULL (the bias comes from rb); args->E is the extent (>= 1).
+ * Supported where rba_attn_prefill runs its two-group bf16 kernel: bf16,
+ * plain K/V, (Hq/Hkv) * min(Sq, 32) > 128, K/V spans of one (batch, kv
+ * head) under 2^31 bytes; otherwise RBA_E_UNSUPPORTED.  Returns
+ * RBA_E_WORKSPACE if workspace is NULL, unaligned (16 bytes) or smaller than
+ * rba_prefill_fused_workspace_bytes(args).  The workspace is scratch: its
+ * contents before and after the call carry no meaning; two calls in flight
+ * at once need two workspaces.                                               */
+rba_status rba_attn_prefill_fused(const rba_attn_args *args, const rba_relbias *rb, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Split-KV count the library picks for `args` on a device with `num_cus`
  * compute units ([V-OPT]: from batch, kv heads and KV length).  num_cus <= 0
  * queries the current device.  Returns >= 1, or 0 if args is invalid.      */

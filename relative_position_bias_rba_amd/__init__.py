@@ -85,6 +85,16 @@ class _PrologueArgs(ctypes.Structure):
     ]
 
 
+class _RelBias(ctypes.Structure):
+    """rba_relbias: relative features and the packed projection of the fused prefill."""
+    _fields_ = [
+        ("r_dim", ctypes.c_int),
+        ("r", ctypes.c_void_p),
+        ("r_s", ctypes.c_int64 * 3),
+        ("PT", ctypes.c_void_p),
+    ]
+
+
 def _load():
     if not os.path.exists(lib_path):
         raise ImportError(
@@ -97,6 +107,14 @@ def _load():
     lib.rba_relproj.restype = ci
     lib.rba_attn_prefill.argtypes = [P, vp]
     lib.rba_attn_prefill.restype = ci
+    lib.rba_relproj_packed_bytes.argtypes = [ci, ci, ci]
+    lib.rba_relproj_packed_bytes.restype = ctypes.c_size_t
+    lib.rba_relproj_pack.argtypes = [ci, ci, ci, vp, vp, vp]
+    lib.rba_relproj_pack.restype = ci
+    lib.rba_prefill_fused_workspace_bytes.argtypes = [P]
+    lib.rba_prefill_fused_workspace_bytes.restype = ctypes.c_size_t
+    lib.rba_attn_prefill_fused.argtypes = [P, ctypes.POINTER(_RelBias), vp, ctypes.c_size_t, vp]
+    lib.rba_attn_prefill_fused.restype = ci
     lib.rba_num_splits.argtypes = [P, ci]
     lib.rba_num_splits.restype = ci
     lib.rba_decode_workspace_bytes.argtypes = [P, ci]
@@ -238,6 +256,76 @@ def attn_prefill(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0, r
     a = make_args(q, k, v, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base,
                   k_scale=k_scale, v_scale=v_scale)
     _check("rba_attn_prefill", _lib.rba_attn_prefill(ctypes.byref(a), _stream(q.device)))
+    return (o, lse) if return_lse else o
+
+
+class PackedProjection:
+    """A projection P [Hq, r_dim, E] repacked by rba_relproj_pack: `data` is the
+    packed bf16 buffer (opaque layout), the shape is kept beside it."""
+
+    def __init__(self, data: torch.Tensor, Hq: int, r_dim: int, E: int):
+        self.data, self.Hq, self.r_dim, self.E = data, Hq, r_dim, E
+
+
+def relproj_pack(P: torch.Tensor) -> PackedProjection:
+    """Repack a bf16 projection P [Hq, r_dim, E] (r_dim a multiple of 16, at
+    most 128) on the GPU into the layout attn_prefill_fused reads.  Pack a
+    weight once and keep the result."""
+    if not P.is_cuda or P.dtype != torch.bfloat16 or P.dim() != 3:
+        raise ValueError("P must be a bf16 [Hq, r_dim, E] GPU tensor")
+    P = P.contiguous()
+    Hq, r_dim, E = P.shape
+    n = _lib.rba_relproj_packed_bytes(Hq, r_dim, E)
+    if n == 0:
+        _check("rba_relproj_pack", RBA_E_UNSUPPORTED)
+    PT = torch.empty(n // 2, dtype=P.dtype, device=P.device)
+    _check("rba_relproj_pack", _lib.rba_relproj_pack(Hq, r_dim, E, _ptr(P), _ptr(PT), _stream(P.device)))
+    return PackedProjection(PT, Hq, r_dim, E)
+
+
+def make_relbias(r: torch.Tensor, PT: PackedProjection, per_head: bool = False) -> _RelBias:
+    """Fill the C relative-feature struct: r [B, Sq, r_dim] shared by the heads,
+    or [B, Sq, Hq, r_dim] with per_head=True; PT from relproj_pack."""
+    if r.stride(-1) != 1:
+        raise ValueError("r: channels must be contiguous")
+    if r.shape[-1] != PT.r_dim:
+        raise ValueError("r_dim mismatch")
+    rb = _RelBias()
+    rb.r_dim = PT.r_dim
+    rb.r, rb.PT = r.data_ptr(), PT.data.data_ptr()
+    rb.r_s[:] = [r.stride(0), r.stride(1), r.stride(2) if per_head else 0]
+    return rb
+
+
+def prefill_fused_workspace_bytes(q, k, v, E: int, *, window=0) -> int:
+    a = make_args(q, k, v, None, q, None, window=window)
+    a.E = int(E)
+    return _lib.rba_prefill_fused_workspace_bytes(ctypes.byref(a))
+
+
+def attn_prefill_fused(q, k, v, r, PT: PackedProjection, *, per_head=False, window=0, scale=None,
+                       log_scale_base=0.0, return_lse=False, out=None, workspace=None):
+    """relproj + attn_prefill in one launch: each workgroup computes the rows
+    of R its query block needs from r and the packed projection PT
+    (relproj_pack) and keeps them in its region of the workspace."""
+    _check_attn_inputs(q, k, v, None)
+    if not (r.is_cuda and PT.data.is_cuda) or r.dtype != q.dtype or PT.data.dtype != q.dtype:
+        raise TypeError("r and PT must be GPU tensors of q's dtype")
+    if PT.Hq != q.shape[2]:
+        raise ValueError("PT was packed for another number of query heads")
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    lse = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=q.device) \
+        if return_lse else None
+    a = make_args(q, k, v, None, o, lse, window=window, scale=scale, log_scale_base=log_scale_base)
+    a.E = PT.E
+    rb = make_relbias(r, PT, per_head)
+    need = _lib.rba_prefill_fused_workspace_bytes(ctypes.byref(a))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    code = _lib.rba_attn_prefill_fused(ctypes.byref(a), ctypes.byref(rb), ctypes.c_void_p(workspace.data_ptr()),
+                                       ws_bytes, _stream(q.device))
+    _check("rba_attn_prefill_fused", code)
     return (o, lse) if return_lse else o
 
 

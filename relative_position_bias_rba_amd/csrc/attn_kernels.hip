@@ -37,6 +37,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -856,6 +857,87 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 // (16-byte chunks XOR-swizzled by row) and read as the PV A-operand with the
 // LDS transpose read, so it never passes through registers.  LDS regions are
 // padded to whole DMA instructions so no lane needs masking.
+// Rows of R for one prefill block, computed in place of reading R ([S-RPB]:
+// the relative logits of a token are its feature r times the head's P).
+// Lane (lc, hh) of wave w serves query column c = 32 w + lc (head hl = c / QB,
+// row qi = c % QB) and computes R[t0 + qi, hkv G + hl, e] for all e; tile eb
+// of 32 distances goes to ws[((hl nEB + eb) QB + qi) 32 + e - 32 eb] (bf16),
+// so the 32 rows of one tile are 2 KB of consecutive stores.  The MFMA
+// operands and their order are those of relproj_kernel (A = rows of P^T in
+// mfma_row_key order, B = r, k-steps ascending, fp32 accumulation, one
+// rounding to bf16), so the values equal rba_relproj's bit for bit.  The A
+// fragments come from the packed projection (relproj_pack_kernel), where the
+// 64 lanes' fragments of one (head, tile, k-step) are 1 KB of consecutive
+// memory.  FK k-steps of 16 channels are held (r_dim <= 16 FK).
+template <int FK>
+__device__ __forceinline__ void bias_rows(const AttnParams &p, __bf16 *ws, int b, int hkv, int t0, int nrows,
+                                          int wave, int lane) {
+    typedef __bf16 T;
+    constexpr int NB = 8 / FK;   // distance tiles per load group; two groups in flight
+    const int lc = lane & 31, hh = lane >> 5;
+    const int col = wave * 32 + lc;
+    const int hl = col / p.QB, qi = col - hl * p.QB;
+    const bool valid = col < p.G * p.QB && qi < nrows;
+    const int hq = hkv * p.G + min(hl, p.G - 1);
+    const int nks = p.r_dim >> 4;
+    const int nEB = (p.E + 31) >> 5;
+    const T *rrow = (const T *)p.rf + (int64_t)b * p.rfs0 + (int64_t)(t0 + (valid ? qi : 0)) * p.rfs1 +
+                    (int64_t)hq * p.rfs2 + 8 * hh;
+    bf16x8 rfr[FK];
+#pragma unroll
+    for (int k = 0; k < FK; ++k) rfr[k] = k < nks ? *(const bf16x8 *)(rrow + 16 * k) : bf16x8{};
+    const int h_lo = (wave * 32) / p.QB;
+    const int h_hi = min((wave * 32 + 31) / p.QB, p.G - 1);
+    for (int hp = h_lo; hp <= h_hi; ++hp) {
+        const T *pt = (const T *)p.PT + (int64_t)(hkv * p.G + hp) * nEB * nks * 512 + lane * 8;
+        const bool mine = valid && hl == hp;
+        T *dst = ws + ((int64_t)hp * nEB * p.QB + qi) * 32 + 16 * hh;
+        auto load = [&](bf16x8 (&a)[NB][FK], int eb0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int k = 0; k < FK; ++k)
+                    a[j][k] = (k < nks && eb0 + j < nEB) ? *(const bf16x8 *)(pt + ((int64_t)(eb0 + j) * nks + k) * 512)
+                                                         : bf16x8{};
+        };
+        auto compute = [&](const bf16x8 (&a)[NB][FK], int eb0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int eb = eb0 + j;
+                if (eb >= nEB) break;
+                f32x16 acc = f32x16{};
+#pragma unroll
+                for (int k = 0; k < FK; ++k)
+                    if (k < nks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][k], rfr[k], acc, 0, 0, 0);
+                if (!mine) continue;
+                bf16x8 w0, w1;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    w0[x] = (__bf16)acc[x];
+                    w1[x] = (__bf16)acc[8 + x];
+                }
+                T *d = dst + (int64_t)eb * p.QB * 32;
+                *(bf16x8 *)d = w0;
+                *(bf16x8 *)(d + 8) = w1;
+            }
+        };
+        // groups of NB tiles alternate between two register sets: the loads of
+        // the next group are in flight while this one is computed
+        bf16x8 a0[NB][FK], a1[NB][FK];
+        load(a0, 0);
+        for (int eb0 = 0; eb0 < nEB; eb0 += 2 * NB) {
+            if (eb0 + NB < nEB) load(a1, eb0 + NB);
+            compute(a0, eb0);
+            if (eb0 + NB >= nEB) break;
+            if (eb0 + 2 * NB < nEB) load(a0, eb0 + 2 * NB);
+            compute(a1, eb0 + NB);
+        }
+    }
+}
+
+// FK = 0: bias rows read from R; FK > 0: computed by bias_rows<FK> into the
+// workgroup's region of bias_ws.
+template <int FK>
 __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParams p_arg) {
     typedef const __attribute__((address_space(4))) AttnParams CParams;
     typedef __bf16 T;
@@ -943,7 +1025,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     const int kb = kt_lo + (int)((int64_t)sp * n_t / p.splits);
     const int ke = kt_lo + (int)((int64_t)(sp + 1) * n_t / p.splits);
     const int ncols = p.G * p.QB;
-    const bool has_bias = p.R != nullptr && p.E > 0;
+    const bool has_bias = (FK > 0 ? p.rf != nullptr : p.R != nullptr) && p.E > 0;
 
     const T *__restrict__ gk = (const T *)p.k + (int64_t)b * p.ks0 + (int64_t)hkv * p.ks2;
     const T *__restrict__ gv = (const T *)p.v + (int64_t)b * p.vs0 + (int64_t)hkv * p.vs2;
@@ -962,6 +1044,19 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     const float bmul = kLog2e * fls;
     const bool wave_active = wave * 32 < ncols;
     const int rb = (prow - N + 1) & ~(CH - 1);
+
+    if constexpr (FK > 0) {
+        if (has_bias) {
+            if (wave_active)
+                bias_rows<FK>(p, (__bf16 *)p.bias_ws + (int64_t)blockIdx.x * p.G * ((p.E + 31) >> 5) * p.QB * 32,
+                              b, hkv, t0, nrows, wave, lane);
+            // the rows are read back by this workgroup's direct-to-LDS loads
+            wait_vmem();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        }
+    }
 
     bf16x8 qf[8];                 // loaded after the first tile's staging is issued
 
@@ -998,10 +1093,19 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     // Slab of group g: chunk L holds chunk L % NCH of the bias window of
     // query column g * HROWS + L / NCH; -j0 is added per tile.
     unsigned svo[2][NSI];
-    const int64_t rbase = (int64_t)b * p.Rs0 + (int64_t)t0 * p.Rs1 + (int64_t)hkv * p.G * p.Rs2;
-    const int64_t rspan = ((int64_t)(nrows - 1) * p.Rs1 + (int64_t)(p.G - 1) * p.Rs2 + p.E) * ES;
-    const rsrc_t rR = make_rsrc(has_bias ? (const T *)p.R + rbase : (const T *)p.q, has_bias ? rspan : 0);
-    const u32x4 rR4 = make_rsrc_words(has_bias ? (const T *)p.R + rbase : (const T *)p.q, has_bias ? rspan : 0);
+    // R rows of this block: from R ([row][head][E] with strides Rs1, Rs2), or
+    // from the workgroup's bias region ([head][tile of 32 distances][row][32]).
+    // Either way a key tile moves every row's window by a fixed byte step.
+    const int nEB = (p.E + 31) >> 5;
+    const bool r_vec = FK > 0 ? true : p.r_vec != 0;
+    const int64_t region = (int64_t)p.G * nEB * p.QB * 32;
+    const T *Rblk = FK > 0 ? (const T *)p.bias_ws + (int64_t)blockIdx.x * region
+                           : (const T *)p.R + ((int64_t)b * p.Rs0 + (int64_t)t0 * p.Rs1 + (int64_t)hkv * p.G * p.Rs2);
+    const int64_t rspan = FK > 0 ? region * ES
+                                 : ((int64_t)(nrows - 1) * p.Rs1 + (int64_t)(p.G - 1) * p.Rs2 + p.E) * ES;
+    const int tshift = FK > 0 ? 2 * p.QB * 32 * ES : N * ES;   // bytes per key tile
+    const rsrc_t rR = make_rsrc(has_bias ? Rblk : (const T *)p.q, has_bias ? rspan : 0);
+    const u32x4 rR4 = make_rsrc_words(has_bias ? Rblk : (const T *)p.q, has_bias ? rspan : 0);
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -1012,7 +1116,10 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
             const bool live = L < HCH && row < ncols && rqi < nrows;
             const int rrb = (p_min + rqi - N + 1) & ~(CH - 1);
             // dead chunks point far past the span: they read zeros
-            svo[g][i] = live ? (unsigned)(((int64_t)rqi * p.Rs1 + (int64_t)rhl * p.Rs2 + rrb + ch * CH) * ES)
+            const int dd = rrb + ch * CH;   // distance of the chunk's first entry at key tile 0
+            const int64_t off = FK > 0 ? (((int64_t)rhl * nEB + (dd >> 5)) * p.QB + rqi) * 32 + (dd & 31)
+                                       : (int64_t)rqi * p.Rs1 + (int64_t)rhl * p.Rs2 + dd;
+            svo[g][i] = live ? (unsigned)(off * ES)
                              : 0x80000000u;
         }
 
@@ -1095,11 +1202,11 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
         rv = tile_rsrc(rv0, vstep, vspan, w1);
         ds0 = t + 1 < n_it && banded(w2);
         s0buf = (t + 1) & 1;
-        s0off = (unsigned)(-w2 * N * ES);
+        s0off = (unsigned)(-w2 * tshift);
         ds1 = t < n_it && banded(w1);
         s1buf = t & 1;
-        s1off = (unsigned)(-w1 * N * ES);
-        if (!p.r_vec) {
+        s1off = (unsigned)(-w1 * tshift);
+        if (!r_vec) {
             if (ds0) slab_fallback(0, s0buf, w2);
             if (ds1) slab_fallback(1, s1buf, w1);
             ds0 = ds1 = false;
@@ -1253,8 +1360,8 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
             rk = tile_rsrc(rk0, kstep, kspan, w1);
             rv = tile_rsrc(rv0, vstep, vspan, w1);
             ds0 = banded(w1);
-            s0off = (unsigned)(-w1 * N * ES);
-            if (ds0 && !p.r_vec) {
+            s0off = (unsigned)(-w1 * tshift);
+            if (ds0 && !r_vec) {
                 slab_fallback(0, 0, w1);
                 ds0 = false;
             }
@@ -1443,6 +1550,20 @@ static int pp_grid(int64_t items) {
     return (items % 8 == 0 && g >= 8 && items > g) ? g : (int)items;
 }
 
+int fused_grid(int64_t items, int cus) {
+    const int64_t g = cus >= 8 ? (cus & ~7) : std::max(cus, 1);
+    return (int)std::min<int64_t>(items, g);
+}
+
+hipError_t launch_attention_fused(const AttnParams &p, int grid, hipStream_t stream) {
+    if (grid <= 0) return hipSuccess;
+    if (p.r_dim <= 64)
+        hipLaunchKernelGGL(attn_prefill_pp_kernel<4>, dim3(grid), dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL(attn_prefill_pp_kernel<8>, dim3(grid), dim3(512), 0, stream, p);
+    return hipGetLastError();
+}
+
 int attn_max_columns(AttnVariant v) { return v == AttnVariant::BF16_WIDE ? 256 : 128; }
 
 hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stream) {
@@ -1464,7 +1585,7 @@ hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stre
             else if (paged)
                 RBA_FWD(__bf16, 8, true, true, false);
             else if (p.kv32)            // two ping-pong groups, one workgroup per CU
-                hipLaunchKernelGGL(attn_prefill_pp_kernel, dim3(pp_grid(blocks)), dim3(512), 0, stream, p);
+                hipLaunchKernelGGL(attn_prefill_pp_kernel<0>, dim3(pp_grid(blocks)), dim3(512), 0, stream, p);
             else
                 RBA_FWD(__bf16, 8, true, false, false);
             break;

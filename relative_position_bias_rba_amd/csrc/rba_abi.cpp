@@ -156,6 +156,27 @@ rba::AttnParams make_params(const rba_attn_args *a, const Plan &pl, int splits) 
     return p;
 }
 
+// rba_attn_prefill_fused runs the two-group bf16 prefill kernel only.
+rba_status fused_supported(const rba_attn_args *a) {
+    const rba_status st = validate_attn(a);
+    if (st != RBA_OK) return st;
+    if (a->R != nullptr || a->E < 1) return RBA_E_INVALID;
+    if (a->dt != RBA_BF16 || a->kv_format != RBA_KV_PLAIN) return RBA_E_UNSUPPORTED;
+    if ((int64_t)a->B * a->Sq == 0) return RBA_OK;   // nothing to do
+    const Plan pl = make_plan(a);
+    if (pl.var != rba::AttnVariant::BF16_WIDE) return RBA_E_UNSUPPORTED;
+    const int64_t kv_row = std::max(a->k_s[1], a->v_s[1]);
+    if (((int64_t)a->Skv * kv_row + kHeadDim) * elem_size(a->dt) >= ((int64_t)1 << 31)) return RBA_E_UNSUPPORTED;
+    return RBA_OK;
+}
+
+size_t fused_workspace(const rba_attn_args *a, const Plan &pl, int cus) {
+    const int64_t items = (int64_t)a->B * a->Hkv * pl.nqb;
+    const int G = a->Hq / a->Hkv;
+    const int64_t tiles = (a->E + 31) / 32;   // the region holds whole tiles of 32 distances
+    return (size_t)rba::fused_grid(items, cus) * pl.QB * G * tiles * 32 * sizeof(uint16_t);
+}
+
 size_t workspace_bytes(const rba_attn_args *a, int splits) {
     if (splits <= 1) return 0;
     const size_t rows = (size_t)a->B * a->Sq * a->Hq;
@@ -189,6 +210,56 @@ rba_status rba_attn_prefill(const rba_attn_args *args, void *stream) {
     const Plan pl = make_plan(args);
     const rba::AttnParams p = make_params(args, pl, 1);
     return rba::launch_attention(p, pl.var, (hipStream_t)stream) == hipSuccess ? RBA_OK : RBA_E_LAUNCH;
+}
+
+size_t rba_relproj_packed_bytes(int Hq, int r_dim, int E) {
+    if (Hq < 1 || r_dim < 1 || E < 1 || r_dim % 16 != 0 || r_dim > 128) return 0;
+    return (size_t)Hq * ((E + 31) / 32) * 32 * r_dim * sizeof(uint16_t);
+}
+
+rba_status rba_relproj_pack(int Hq, int r_dim, int E, const void *P, void *PT, void *stream) {
+    if (Hq < 1 || r_dim < 1 || E < 1) return RBA_E_INVALID;
+    if (r_dim % 16 != 0 || r_dim > 128) return RBA_E_UNSUPPORTED;
+    if (P == nullptr || PT == nullptr || !aligned(P, 16) || !aligned(PT, 16)) return RBA_E_INVALID;
+    if ((int64_t)Hq > 65535) return RBA_E_UNSUPPORTED;
+    return rba::launch_relproj_pack(Hq, r_dim, E, P, PT, (hipStream_t)stream) == hipSuccess ? RBA_OK
+                                                                                             : RBA_E_LAUNCH;
+}
+
+size_t rba_prefill_fused_workspace_bytes(const rba_attn_args *args) {
+    if (fused_supported(args) != RBA_OK) return 0;
+    const int cus = device_cus();
+    if (cus <= 0) return 0;
+    return fused_workspace(args, make_plan(args), cus);
+}
+
+rba_status rba_attn_prefill_fused(const rba_attn_args *args, const rba_relbias *rb, void *workspace,
+                                  size_t workspace_bytes_, void *stream) {
+    rba_status st = fused_supported(args);
+    if (st != RBA_OK) return st;
+    if (rb == nullptr) return RBA_E_INVALID;
+    if (rb->r_dim < 1) return RBA_E_INVALID;
+    if (rb->r_dim % 16 != 0 || rb->r_dim > 128) return RBA_E_UNSUPPORTED;
+    if ((int64_t)args->B * args->Sq == 0) return RBA_OK;
+    if (rb->r == nullptr || rb->PT == nullptr || !aligned(rb->r, 16) || !aligned(rb->PT, 16)) return RBA_E_INVALID;
+    if (!strides_ok(rb->r_s, 8)) return RBA_E_INVALID;
+    if (rb->r_s[2] != 0 && rb->r_s[2] < rb->r_dim) return RBA_E_INVALID;
+    const int cus = device_cus();
+    if (cus <= 0) return RBA_E_LAUNCH;
+    const Plan pl = make_plan(args);
+    const size_t need = fused_workspace(args, pl, cus);
+    if (workspace == nullptr || workspace_bytes_ < need || !aligned(workspace, 16)) return RBA_E_WORKSPACE;
+    rba::AttnParams p = make_params(args, pl, 1);
+    p.E = args->E;
+    p.rf = rb->r;
+    p.rfs0 = rb->r_s[0], p.rfs1 = rb->r_s[1], p.rfs2 = rb->r_s[2];
+    p.r_dim = rb->r_dim;
+    p.PT = rb->PT;
+    p.bias_ws = workspace;
+    const int64_t items = (int64_t)args->B * args->Hkv * pl.nqb;
+    return rba::launch_attention_fused(p, rba::fused_grid(items, cus), (hipStream_t)stream) == hipSuccess
+               ? RBA_OK
+               : RBA_E_LAUNCH;
 }
 
 int rba_num_splits(const rba_attn_args *args, int num_cus) {

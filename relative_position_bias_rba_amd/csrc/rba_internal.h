@@ -40,6 +40,16 @@ struct AttnParams {
     // (bytes) laid out like k and v (paged: page, key, head).
     const uint8_t *k_scale, *v_scale;
     int64_t kss0, kss1, kss2, vss0, vss1, vss2;
+    // Relative logits computed inside the prefill kernel (rf != null; then
+    // R is null): relative features rf [B, Sq, (Hq,) r_dim] with strides
+    // rfs0..2 (rfs2 = 0: shared by the heads), the projection packed by
+    // launch_relproj_pack, and bias_ws, G*ceil(E/32)*QB*32 bf16 entries per
+    // workgroup of the grid, where each block's rows of R are kept.
+    const void *rf;
+    int64_t rfs0, rfs1, rfs2;
+    int r_dim;
+    const void *PT;
+    void *bias_ws;
 };
 
 // One attention-prologue launch (ShortConv, RMSNorm, cache write) for T new
@@ -70,6 +80,19 @@ enum class AttnVariant { BF16_WIDE, BF16_NARROW, FP32 };
 int attn_max_columns(AttnVariant v);
 
 hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stream);
+
+// The prefill kernel with the relative logits computed in place (p.rf set):
+// `grid` workgroups, each owning bias_ws rows QB*G*E of its own.
+hipError_t launch_attention_fused(const AttnParams &p, int grid, hipStream_t stream);
+
+// Workgroups the fused prefill kernel runs with for `items` work items on a
+// device with `cus` compute units (the bias workspace holds one region each).
+int fused_grid(int64_t items, int cus);
+
+// The projection P [Hq, r_dim, E] (bf16, r_dim a multiple of 16) packed as
+// MFMA A-operand fragments for the prefill kernel: Hq*ceil(E/32)*32*r_dim
+// entries.
+hipError_t launch_relproj_pack(int Hq, int r_dim, int E, const void *P, void *PT, hipStream_t stream);
 
 hipError_t launch_combine(const float *o_part, const float *lse_part, int splits, int B, int Sq, int Hq,
                           void *o, bool o_bf16, int64_t os0, int64_t os1, int64_t os2, float *lse,

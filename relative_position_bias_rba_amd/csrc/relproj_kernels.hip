@@ -237,7 +237,36 @@ __global__ __launch_bounds__(NT) void relproj_kernel(const TI *__restrict__ r, i
     }  // token blocks
 }
 
+// The projection packed as MFMA A-operand fragments for the prefill kernel
+// that computes its own R rows: for head h, tile eb of 32 distances, k-step k
+// (channels 16k..16k+15) and lane l = (lc = l % 32, hh = l / 32), the 8
+// entries P[h, 16k + 8hh + x, 32 eb + mfma_row_key(lc)], x = 0..7, at
+// PT[(((h nEB + eb) nks + k) 64 + l) 8 + x] (zero past E).  One workgroup
+// per (tile, head); bf16.
+__global__ __launch_bounds__(256) void relproj_pack_kernel(const __bf16 *__restrict__ P, __bf16 *__restrict__ PT,
+                                                           int r_dim, int E) {
+    const int eb = blockIdx.x, h = blockIdx.y, nEB = gridDim.x;
+    const int nks = r_dim >> 4;
+    const __bf16 *src = P + (int64_t)h * r_dim * E;
+    for (int idx = threadIdx.x; idx < nks * 64; idx += blockDim.x) {
+        const int k = idx >> 6, l = idx & 63;
+        const int e = 32 * eb + mfma_row_key(l & 31);
+        const int c0 = 16 * k + 8 * (l >> 5);
+        bf16x8 v;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) v[x] = e < E ? src[(int64_t)(c0 + x) * E + e] : (__bf16)0.f;
+        *(bf16x8 *)(PT + ((((int64_t)h * nEB + eb) * nks + k) * 64 + l) * 8) = v;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_relproj_pack(int Hq, int r_dim, int E, const void *P, void *PT, hipStream_t stream) {
+    if (Hq <= 0 || r_dim <= 0 || E <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((E + 31) / 32), (unsigned)Hq);
+    hipLaunchKernelGGL(relproj_pack_kernel, grid, dim3(256), 0, stream, (const __bf16 *)P, (__bf16 *)PT, r_dim, E);
+    return hipGetLastError();
+}
 
 hipError_t launch_relproj(bool in_bf16, bool out_bf16, int64_t T, int Hq, int r_dim, int E, const void *r,
                           int64_t r_stride, int64_t r_stride_h, const void *P, void *R, hipStream_t stream) {

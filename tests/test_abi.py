@@ -331,6 +331,79 @@ def test_relproj_validation():
     assert lib.rba_relproj(1, 1, 8, 4, 64, 16, pr, 256, -64, pP, pR, None) == RBA_E_INVALID
 
 
+def test_relproj_pack_validation():
+    assert lib.rba_relproj_packed_bytes(4, 64, 16) == 4 * 32 * 64 * 2      # E padded to whole 32-tiles
+    assert lib.rba_relproj_packed_bytes(4, 64, 33) == 4 * 64 * 64 * 2
+    assert lib.rba_relproj_packed_bytes(4, 40, 16) == 0                   # r_dim not a multiple of 16
+    assert lib.rba_relproj_packed_bytes(4, 144, 16) == 0
+    assert lib.rba_relproj_packed_bytes(0, 64, 16) == 0
+    P = torch.zeros(4, 64, 16, dtype=torch.bfloat16)
+    PT = torch.zeros(4, 32, 64, dtype=torch.bfloat16)
+    pP, pT = ctypes.c_void_p(P.data_ptr()), ctypes.c_void_p(PT.data_ptr())
+    assert lib.rba_relproj_pack(4, 40, 16, pP, pT, None) == RBA_E_UNSUPPORTED
+    assert lib.rba_relproj_pack(0, 64, 16, pP, pT, None) == RBA_E_INVALID
+    assert lib.rba_relproj_pack(4, 0, 16, pP, pT, None) == RBA_E_INVALID
+    assert lib.rba_relproj_pack(4, 64, 0, pP, pT, None) == RBA_E_INVALID
+    assert lib.rba_relproj_pack(4, 64, 16, None, pT, None) == RBA_E_INVALID
+    assert lib.rba_relproj_pack(4, 64, 16, pP, ctypes.c_void_p(PT.data_ptr() + 2), None) == RBA_E_INVALID
+
+
+def _fused_args(Sq=64, Hq=16, Hkv=2, E=64, dtype=torch.bfloat16):
+    q, k, v, _, o = _tensors(B=1, Sq=Sq, Skv=Sq, Hq=Hq, Hkv=Hkv, E=E, dtype=dtype)
+    a = make_args(q, k, v, None, o, None)
+    a.E = E
+    r = torch.zeros(1, Sq, 64, dtype=dtype)
+    PT = rba.PackedProjection(torch.zeros(Hq * E * 64, dtype=dtype), Hq, 64, E)
+    rb = rba.make_relbias(r, PT)
+    return a, rb, (q, k, v, o, r, PT.data)
+
+
+def _fused(a, rb, ws=None, nbytes=0):
+    return lib.rba_attn_prefill_fused(ctypes.byref(a), None if rb is None else ctypes.byref(rb), ws, nbytes, None)
+
+
+def test_prefill_fused_validation():
+    """Rejections that the host decides before it asks the device anything."""
+    a, rb, keep = _fused_args()
+    assert _fused(a, None) == RBA_E_INVALID
+    R = torch.zeros(1, 64, 16, 64, dtype=torch.bfloat16)
+    a.R = R.data_ptr()                                   # the bias comes from r, not from R
+    a.R_s[:] = [R.stride(0), R.stride(1), R.stride(2)]
+    assert _fused(a, rb) == RBA_E_INVALID
+    a, rb, keep = _fused_args()
+    a.E = 0
+    assert _fused(a, rb) == RBA_E_INVALID
+    a, rb, keep = _fused_args()
+    rb.r_dim = 40
+    assert _fused(a, rb) == RBA_E_UNSUPPORTED               # r_dim must be a multiple of 16
+    rb.r_dim = 144
+    assert _fused(a, rb) == RBA_E_UNSUPPORTED
+    rb.r_dim = 0
+    assert _fused(a, rb) == RBA_E_INVALID
+    a, rb, keep = _fused_args(Hq=8, Hkv=2)                  # 4 heads x 32 rows: the 4-wave kernel
+    assert _fused(a, rb) == RBA_E_UNSUPPORTED
+    a, rb, keep = _fused_args(dtype=torch.float32)
+    assert _fused(a, rb) == RBA_E_UNSUPPORTED
+    a, rb, keep = _fused_args()
+    rb.r = None
+    assert _fused(a, rb) == RBA_E_INVALID
+    a, rb, keep = _fused_args()
+    rb.PT = keep[5].data_ptr() + 2
+    assert _fused(a, rb) == RBA_E_INVALID
+    a, rb, keep = _fused_args()
+    rb.r_s[1] = 60                                       # token stride not a multiple of 8
+    assert _fused(a, rb) == RBA_E_INVALID
+    a, rb, keep = _fused_args()
+    rb.r_s[2] = 32                                       # per-head stride below r_dim
+    assert _fused(a, rb) == RBA_E_INVALID
+    a, rb, keep = _fused_args()
+    a.Sq = a.B = 0
+    assert _fused(a, rb) == RBA_OK                          # nothing to do
+    a, rb, keep = _fused_args()
+    a.Hkv = 5                                            # Hq not a multiple of Hkv
+    assert _fused(a, rb) == RBA_E_INVALID
+
+
 # --------------------------------------------------------------------------- split heuristic (host logic)
 
 def _split_args(B, Sq, Skv, Hq=64, Hkv=8, window=0):
