@@ -36,7 +36,7 @@ def log(*a):
 # HBM bytes per launch of the prefill kernel: rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors
 # from a plain 1 GiB device copy under the same counters), keyed by the sha256 prefix of the kernel
 # source the counters were taken on; any other source reports null.
-PROFILED_TRAFFIC = {"53b732c7cd7cfc39": 510326 * 1024 * 2 + 131408 * 1024}
+PROFILED_TRAFFIC = {"792606d433407a28": 510155 * 1024 * 2 + 131408 * 1024}
 
 
 def kernel_source_hash():
@@ -442,7 +442,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": PROFILED_TRAFFIC.get(kernel_source_hash()),
-                     "kernel": "attn_prefill_pp_kernel", "avg_ms": round(ms_attn, 4),
+                     "kernel": "attn_prefill_pp_kernel<0>", "avg_ms": round(ms_attn, 4),
                      "algorithmic_flops": flops},
         "kernels": {"attn_prefill_ms": round(ms_attn, 4), "attn_prefill_tflops": round(attn_tflops, 2),
                     "relproj_ms": round(ms_relproj, 4),
