@@ -1041,7 +1041,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     // log-scale factor, kept > 0 so that masked -inf logits stay -inf
     const float fls = p.inv_ln_base > 0.f ? fmaxf(logf((float)prow + 1.f) * p.inv_ln_base, 1e-30f) : 1.f;
     const float amul = p.scale_log2e * fls;
-    const float bmul = kLog2e * fls;
+    const float bsc = kLog2e / p.scale_log2e;   // 1 / scale: the bias in units of the raw dot product
     const bool wave_active = wave * 32 < ncols;
     const int rb = (prow - N + 1) & ~(CH - 1);
 
@@ -1295,11 +1295,20 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
 #pragma unroll
             for (int u = 0; u < KT; ++u) {
                 if (band) {
+                    // entries r = 0..7 of sub-tile u are the 8 bf16 ending at
+                    // sr - 32u (reversed), r = 8..15 the 8 ending at sr - 32u - 8;
+                    // added in the unscaled domain (s + bias / scale), scaled
+                    // with the dot product in the exponent below
+                    bf16x8 braw[2];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float bias = __builtin_bit_cast(float, (unsigned)__builtin_bit_cast(unsigned short, sr[-(32 * u + r)]) << 16);
-                        if (partial) bias = (32 * u + r > elim) ? bias : 0.f;
-                        S[u][r] = fmaf(bias, bmul, S[u][r] * amul);
+                    for (int h8 = 0; h8 < 2; ++h8) __builtin_memcpy(&braw[h8], sr - 32 * u - 8 * h8 - 7, 16);
+                    if (partial) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            S[u][r] = fmaf(32 * u + r > elim ? (float)braw[r >> 3][7 - (r & 7)] : 0.f, bsc, S[u][r]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) S[u][r] = fmaf((float)braw[r >> 3][7 - (r & 7)], bsc, S[u][r]);
                     }
                 }
                 if (edge) {
@@ -1318,7 +1327,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
 #pragma unroll
             for (int r = 0; r < 16; ++r) mt = fmaxf(mt, S[u][r]);
         burst(6, 11);
-        if (!band) mt *= amul;
+        mt *= amul;
         mt = max_across_halves(mt);
         // The reference max only moves when the tile max exceeds it by more
         // than kRescaleSlack (alpha = 1 otherwise).
@@ -1329,7 +1338,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
         l *= alpha;
         o_scale = alpha;        // applied to O at the start of the next matrix phase
         const float mu = m == -INFINITY ? 0.f : m;
-        const float sa = band ? 1.f : amul;
+        const float sa = amul;
         float sum = 0.f;
 #pragma unroll
         for (int u = 0; u < KT; ++u)
