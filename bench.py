@@ -301,12 +301,22 @@ def full_prefill_leg(rba, torch, reps=5):
                                      ctypes.c_void_p(r2.data_ptr()), r2.stride(0), 0,
                                      ctypes.c_void_p(d["P"].data_ptr()), ctypes.c_void_p(R.data_ptr()),
                                      rba._stream(o.device)), reps, torch)
+    # the same step with the projection computed inside the prefill kernel
+    PT = rba.relproj_pack(d["P"])
+    af = rba.make_args(d["q"], d["k"], d["v"], None, o, None, window=w.window, log_scale_base=w.log_scale_base)
+    af.E = w.E
+    rb = rba.make_relbias(d["r"], PT)
+    need = rba._lib.rba_prefill_fused_workspace_bytes(ctypes.byref(af))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ms_f = time_launches(c_launcher(rba, "rba_attn_prefill_fused", ctypes.byref(af), ctypes.byref(rb),
+                                    ctypes.c_void_p(ws.data_ptr()), need, rba._stream(o.device)), reps, torch)
     flops = w.attn_flops()
     res = {"attn_ms": round(ms, 3), "attn_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
            "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
            "relproj_ms": round(ms_rp, 3), "step_tflops": round(flops / ((ms + ms_rp) * 1e-3) / 1e12, 1),
+           "fused_ms": round(ms_f, 3), "fused_step_tflops": round(flops / (ms_f * 1e-3) / 1e12, 1),
            "algorithmic_flops": flops, "timing": "back-to-back mean after a clock warm-up"}
-    del d, R, o
+    del d, R, o, ws, PT
     torch.cuda.empty_cache()
     return res
 

@@ -152,6 +152,15 @@ def test_fused_full_size_workload_bitwise_and_sampled():
         check(f"full-size row {t} o", of[:, t:t + 1], wo)
 
 
+def test_fused_full_causal_workload_bitwise():
+    """The full-causal workload (B=2, S=32768, log-scale 4096): 16,384 blocks,
+    64 rounds per workgroup; bit for bit the two-kernel path."""
+    w = CONFIGS["c3_full_prefill"]
+    d = {k: v.to(DEV) for k, v in make_inputs(w).items()}
+    (of, lf), (ou, lu) = both_paths(d, w, d["r"], False)
+    assert torch.equal(of, ou) and torch.equal(lf, lu)
+
+
 def test_fused_workspace_checks_and_reuse():
     """Too small or missing workspace is refused before any launch; a workspace
     reused across calls (stale rows of an earlier call in it) changes nothing."""
