@@ -103,6 +103,8 @@ FUSED_CASES = [
     ("per_head_r", dict(B=1, Sq=200, Skv=200, Hq=16, Hkv=2, window=0, E=64, r_dim=32), True),
     ("rows_17_r16", dict(B=1, Sq=17, Skv=17, Hq=8, Hkv=1, window=0, E=8, r_dim=16), False),
     ("extent_past_seq", dict(B=1, Sq=40, Skv=40, Hq=16, Hkv=2, window=0, E=512), False),
+    ("extent_1000_swa", dict(B=1, Sq=700, Skv=700, Hq=16, Hkv=2, window=300, E=1000), False),
+    ("extent_2050_r128", dict(B=1, Sq=300, Skv=2300, Hq=16, Hkv=2, window=0, E=2050, r_dim=128), False),
 ]
 
 
