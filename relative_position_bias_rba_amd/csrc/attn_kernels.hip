@@ -8,7 +8,13 @@
 // "相対位置バイアス付き Attention"; GQA with head size 128 from "vLLM TML
 // Inkling サポート", section "TML Inkling モデルアーキテクチャ").
 //
-// Design (one kernel serves prefill and split-KV decode):
+// Two kernels share the arithmetic below: attn_fwd_kernel (split-KV decode,
+// paged and MXFP8 K/V, narrow and fp32 shapes) and attn_prefill_pp_kernel
+// (bf16 prefill: two groups of four waves alternate between matrix and vector
+// phases, one persistent workgroup per CU; its FK > 0 instances compute the
+// block's rows of R themselves from r and the packed projection).
+//
+// Design:
 //  * A workgroup of NW waves owns one (batch, kv head, block of QB query rows,
 //    key-range split) and all G query heads of that kv head.  Its G*QB query
 //    columns form 32-column tiles, one per wave, and all of them read the K/V
