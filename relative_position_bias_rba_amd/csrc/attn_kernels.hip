@@ -153,12 +153,15 @@ __device__ __forceinline__ u32x4 make_rsrc_words(const void *base, int64_t bytes
 // it never makes later LDS reads wait for it (it cannot tell which LDS bytes
 // a direct-to-LDS load writes and would otherwise wait for all of them);
 // the caller waits (vmcnt(0)) before the barrier that hands the data over.
+// The LDS address is an operand bound to m0, so the compiler writes m0 itself
+// (m0 is reserved to it: the assembly must not write it); the s_nop is the
+// wait state an LDS DMA needs after an m0 write.
 __device__ __forceinline__ void dma16_untracked(u32x4 rsrc, unsigned voff, const void *lds_wave) {
     const unsigned m0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void *)lds_wave;
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
-                 : "v"(voff), "s"(rsrc), "s"(m0)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(rsrc), "{m0}"(m0)
+                 : "memory");
 }
 
 // E8M0 scale code -> its power of two (code 0 is 2^-127, an fp32 subnormal).
