@@ -579,3 +579,43 @@ def test_prologue_sequence_start_ignores_history_and_places_rows():
     assert list(a[3]) == [8, 9, 0, 1, 2]
     # V of the first row of sequence 1 is tap 0 times the row itself
     assert np.allclose(a[2][2], wv[:, 0].reshape(2, 8) * v[2], rtol=0, atol=1e-12)
+
+
+def test_prologue_composition_closed_forms():
+    """The order of the prologue's steps, from values worked out by hand.
+
+    K is convolved first and normalised after ("SGLang と Miles が Inkling を
+    初日からサポート", section "Inkling のモデルアーキテクチャ": the K
+    ShortConv sits between the K projection and the Q/K normalisation); V is
+    convolved only; q is normalised with its own weight.  With taps 1 on the
+    current row and on the row one position back, a history row u and a new
+    row c*u (c > 0):
+      * convolve then normalise: g_k * (1+c)u / rms((1+c)u) = g_k * u / rms(u);
+      * normalise then convolve would give 2 * g_k * u / rms(u).
+    u alternates +-1, so rms(u) = 1 and the K row must equal g_k * u exactly;
+    the V row (taps the same) must equal (1+c) * w for history row w and new
+    row c*w.  A constant q row 3 normalises to g_q exactly (eps = 0), which
+    tells g_q from g_k."""
+    Hq, Hkv, d, W = 2, 1, 8, 4
+    c = 3.0
+    u = np.array([1.0, -1.0] * (d // 2))
+    w = np.arange(1.0, d + 1.0)
+    gq = np.linspace(0.5, 1.2, d)
+    gk = np.linspace(2.0, -1.0, d)
+    taps = np.zeros((Hkv * d, W))
+    taps[:, 0] = 1.0
+    taps[:, 1] = 1.0
+    sk = np.zeros((1, W - 1, Hkv, d))
+    sv = np.zeros((1, W - 1, Hkv, d))
+    sk[0, W - 2, 0] = u          # the row one position before the new token
+    sv[0, W - 2, 0] = w
+    sk[0, 0, 0] = 50.0           # three back: tap 0 there, so it must not show
+    q = np.full((1, Hq, d), 3.0)
+    k = (c * u).reshape(1, Hkv, d)
+    v = (c * w).reshape(1, Hkv, d)
+    q_out, k_rows, v_rows, pos, _, _ = attention_prologue(q, k, v, [0, 1], [10], taps, taps, gq, gk, 0.0, sk, sv)
+    assert np.allclose(k_rows[0, 0], gk * u, rtol=0, atol=1e-14)
+    assert not np.allclose(k_rows[0, 0], 2.0 * gk * u, rtol=0, atol=1e-3)
+    assert np.allclose(v_rows[0, 0], (1.0 + c) * w, rtol=0, atol=1e-13)
+    assert np.allclose(q_out[0], np.broadcast_to(gq, (Hq, d)), rtol=0, atol=1e-14)
+    assert list(pos) == [9]
