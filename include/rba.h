@@ -189,13 +189,19 @@ rba_status rba_attn_prefill_fused(const rba_attn_args *args, const rba_relbias *
 int rba_num_splits(const rba_attn_args *args, int num_cus);
 
 /* Bytes of workspace rba_attn_decode needs for `num_splits` splits
- * (0 = the heuristic's choice on the current device).  0 when one split is
+ * (0 = the heuristic's choice on the current device; split-KV decode as in
+ * [V-OPT], "vLLM TML Inkling サポート", section
+ * "低レイテンシコレクティブとカーネル").  0 when one split is
  * used (no workspace needed).  Layout: fp32 partial outputs
  * [splits][B][Sq][Hq][d] followed by fp32 partial lse [splits][B][Sq][Hq].  */
 size_t rba_decode_workspace_bytes(const rba_attn_args *args, int num_splits);
 
-/* Split-KV attention for a few query rows against a long cache: each split
- * covers a contiguous range of key tiles and writes its normalised partial
+/* Split-KV attention for a few query rows against a long cache ([V-OPT]:
+ * the attention splits the key range, with the split count chosen per batch
+ * and KV length; "vLLM TML Inkling サポート", section
+ * "低レイテンシコレクティブとカーネル"); the scores are those of
+ * rba_attn_prefill ([S-RPB]).  Each split covers a contiguous range of key
+ * tiles and writes its normalised partial
  * output and lse into `workspace`; rba_splitkv_combine then merges them on
  * the same stream.  num_splits = 0 uses rba_num_splits; 1 writes o directly.
  * Returns RBA_E_WORKSPACE if workspace is NULL or too small when needed.   */
@@ -295,7 +301,10 @@ typedef struct rba_prologue_args {
 rba_status rba_attn_prologue(const rba_prologue_args *args, const rba_attn_args *cache, const rba_paged_kv *paged,
                              void *stream);
 
-/* Merge split partials into args->o (and args->lse if non-NULL):
+/* Merge split partials into args->o (and args->lse if non-NULL); the
+ * combine step of [V-OPT]'s split-KV decode ("vLLM TML Inkling サポート",
+ * section "低レイテンシコレクティブとカーネル"), exact because each split's
+ * softmax is renormalised by its lse:
  *   M = max_s lse_s;  w_s = exp(lse_s - M);  o = sum_s w_s o_s / sum_s w_s;
  *   lse = M + ln sum_s w_s.  Splits with lse = -inf get weight 0; a row whose
  *   splits are all empty gets o = 0, lse = -inf.

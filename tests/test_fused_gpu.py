@@ -39,8 +39,11 @@ def check(name, got, want, tol_max=2e-2, tol_mean=2e-3):
     assert g.shape == w.shape, (g.shape, w.shape)
     assert np.all(np.isfinite(g)), f"{name}: non-finite output"
     d = np.abs(g - w)
-    say(f"[{name}] max|d|={d.max():.3e} mean|d|={d.mean():.3e}")
+    rel = float(np.linalg.norm(g - w) / max(np.linalg.norm(w), 1e-30))
+    say(f"[{name}] max|d|={d.max():.3e} mean|d|={d.mean():.3e} rel_l2={rel:.3e}")
     assert d.max() <= tol_max and d.mean() <= tol_mean, name
+    # relative L2: 1e-2 on bf16 outputs, 2e-3 on lse (looser mean bound given)
+    assert rel <= (1e-2 if tol_mean <= 2e-3 else 2e-3), f"{name}: rel_l2 {rel:.3e}"
 
 
 def per_head_r(inp, w, seed):

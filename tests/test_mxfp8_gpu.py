@@ -41,11 +41,14 @@ def check(name, got, want, fp32=False, tol=None):
     assert np.all(np.isfinite(g)), f"{name}: non-finite output"
     d = np.abs(g - w)
     mx, mean = float(d.max()), float(d.mean())
-    say(f"[{name}] max|d|={mx:.3e} mean|d|={mean:.3e}")
+    rel = float(np.linalg.norm(g - w) / max(np.linalg.norm(w), 1e-30))
+    say(f"[{name}] max|d|={mx:.3e} mean|d|={mean:.3e} rel_l2={rel:.3e}")
     if fp32:
         assert mx <= (1e-5 if tol is None else tol), name
+        assert rel <= (1e-5 if tol is None else 2e-3), f"{name}: rel_l2 {rel:.3e}"
     else:
         assert mx <= 2e-2 and mean <= 2e-3, name
+        assert rel <= 1e-2, f"{name}: rel_l2 {rel:.3e}"
 
 
 def quantize_cpu(x):

@@ -1,7 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
 Tolerances: fp32 paths max|d| <= 1e-5; bf16 paths max|d| <= 2e-2 and
-mean|d| <= 2e-3; masking and bucket indexing exact (one-hot tests).
+mean|d| <= 2e-3, relative L2 <= 1e-2 (lse 2e-3); masking and bucket indexing
+exact (one-hot tests); biased outputs must sit far closer to the oracle than
+the oracle without bias does.
 Small cases compare every output element; the full-size workloads run in the
 launch configuration the benchmark times and compare sampled rows.
 """
@@ -32,6 +34,10 @@ def say(*a):
 
 
 def check(name, got, want, fp32, extra_tol=None):
+    """Element-wise comparison.  Absolute bounds as stated at the top, plus a
+    relative L2 bound: 1e-5 on fp32 paths, 1e-2 on bf16 outputs (one bf16
+    rounding of o and of the probabilities is ~4e-3) and 2e-3 on the fp32 lse
+    of bf16 paths (lse is O(ln n))."""
     g = got.detach().double().cpu().numpy() if hasattr(got, "detach") else np.asarray(got, np.float64)
     w = np.asarray(want, np.float64)
     assert g.shape == w.shape, (g.shape, w.shape)
@@ -42,9 +48,28 @@ def check(name, got, want, fp32, extra_tol=None):
     say(f"[{name}] max|d|={mx:.3e} mean|d|={mean:.3e} rel_l2={rel:.3e}")
     if fp32:
         assert mx <= (1e-5 if extra_tol is None else extra_tol), name
+        assert rel <= (1e-5 if extra_tol is None else 2e-3), f"{name}: rel_l2 {rel:.3e}"
     else:
         assert mx <= 2e-2 and mean <= 2e-3, name
+        assert rel <= 1e-2, f"{name}: rel_l2 {rel:.3e}"
     return mx, mean
+
+
+def check_bias_seen(name, got, want, want_nobias, ratio=0.1):
+    """The output must follow the bias: its distance to the biased oracle is
+    at most `ratio` times the distance between the biased and the unbiased
+    oracle (a kernel that dropped or misplaced the bias would sit about as far
+    from the biased oracle as the unbiased one does).  Skipped where the bias
+    cannot move the output (e.g. one visible key per row)."""
+    g = got.detach().double().cpu().numpy() if hasattr(got, "detach") else np.asarray(got, np.float64)
+    w, w0 = np.asarray(want, np.float64), np.asarray(want_nobias, np.float64)
+    effect = float(np.linalg.norm(w - w0))
+    if effect <= 1e-3 * max(float(np.linalg.norm(w)), 1e-30):
+        say(f"[{name}] bias effect {effect:.3e}: too small to test")
+        return
+    r = float(np.linalg.norm(g - w)) / effect
+    say(f"[{name}] |got - oracle| / |oracle - oracle(R=0)| = {r:.3e}")
+    assert r <= ratio, f"{name}: the output does not follow the bias ({r:.3e})"
 
 
 def to_dev(inp):
@@ -214,6 +239,52 @@ def test_prefill_bf16_small(name, over):
     wo, wl = oracle_full(inp, w)
     check(f"{name} o", o, wo, False)
     check(f"{name} lse", lse, wl, True, extra_tol=2e-2)
+    wo0, _ = oracle.attention(inp["q"], inp["k"], inp["v"], None, window=w.window, log_scale_base=w.log_scale_base)
+    check_bias_seen(f"{name} bias", o, wo, wo0)
+
+
+def _strided_R(R, layout):
+    """R [B, Sq, Hq, E] in a layout whose rows are not 16-byte aligned:
+    'wide' = a view into rows of E + 3 entries, 'offset' = a view starting
+    3 entries into each row (the base pointer itself unaligned)."""
+    B, Sq, Hq, E = R.shape
+    big = torch.full((B, Sq, Hq, E + 3), float("nan"), dtype=R.dtype, device=R.device)
+    view = big[..., :E] if layout == "wide" else big[..., 3:]
+    view.copy_(R)
+    return view
+
+
+UNALIGNED_CASES = [
+    # name, overrides of the windowed bf16 workload (G = 8: the two-group prefill kernel), R layout
+    ("ext100_full", dict(B=1, Sq=333, Skv=333, Hq=16, Hkv=2, window=0, E=100), "contiguous"),
+    ("ext100_swa", dict(B=2, Sq=300, Skv=300, Hq=16, Hkv=2, window=96, E=100), "contiguous"),
+    ("ext64_wide_rows", dict(B=1, Sq=260, Skv=260, Hq=16, Hkv=2, window=0, E=64), "wide"),
+    ("ext72_offset", dict(B=1, Sq=200, Skv=270, Hq=16, Hkv=2, window=150, E=72,
+                          log_scale_base=64.0), "offset"),
+]
+
+
+@pytest.mark.parametrize("name,over,layout", UNALIGNED_CASES, ids=[c[0] for c in UNALIGNED_CASES])
+def test_prefill_unaligned_bias_rows(name, over, layout):
+    """Bias rows that are not 16-byte aligned (extent not a multiple of 8, or
+    a strided / offset view of R): the prefill kernel stages them with element
+    loads instead of direct-to-LDS copies."""
+    m = rba()
+    w = small(CONFIGS["c2_swa_prefill"], **over)
+    say(f"prefill unaligned bias {name} ({layout}): {w}")
+    inp = make_inputs(w)
+    d = to_dev(inp)
+    R = m.relproj(d["r"], d["P"])
+    if layout != "contiguous":
+        R = _strided_R(R, layout)
+    o, lse = m.attn_prefill(d["q"], d["k"], d["v"], R, window=w.window, log_scale_base=w.log_scale_base,
+                            return_lse=True)
+    torch.cuda.synchronize()
+    wo, wl = oracle_full(inp, w)
+    check(f"{name} o", o, wo, False)
+    check(f"{name} lse", lse, wl, True, extra_tol=2e-2)
+    wo0, _ = oracle.attention(inp["q"], inp["k"], inp["v"], None, window=w.window, log_scale_base=w.log_scale_base)
+    check_bias_seen(f"{name} bias", o, wo, wo0)
 
 
 def test_prefill_kv_spans_beyond_31_bits():
@@ -237,6 +308,38 @@ def test_prefill_kv_spans_beyond_31_bits():
     wo, wl = oracle_full(inp, w)
     check("large-stride o", o, wo, False)
     check("large-stride lse", lse, wl, True, extra_tol=2e-2)
+    # the same kernel with bias rows that are not 16-byte aligned (element loads)
+    Ru = _strided_R(R, "wide")
+    o2, lse2 = m.attn_prefill(d["q"], kv[0], kv[1], Ru, window=w.window, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(lse2, lse)
+    del kv, buf
+    torch.cuda.empty_cache()
+
+
+def test_prefill_kv_spans_beyond_31_bits_unaligned_extent():
+    """The 64-bit-offset prefill with an extent of 100 (bias rows not 16-byte
+    aligned) against the oracle."""
+    m = rba()
+    w = small(CONFIGS["c2_swa_prefill"], B=1, Sq=200, Skv=200, Hq=16, Hkv=2, window=0, E=100)
+    say(f"prefill with 8 MiB K/V row stride, E=100: {w}")
+    inp = make_inputs(w)
+    d = to_dev(inp)
+    rs = 1 << 22
+    kv = []
+    for name in ("k", "v"):
+        buf = torch.empty(w.Skv * rs, dtype=torch.bfloat16, device=DEV)
+        view = buf.as_strided((w.B, w.Skv, w.Hkv, w.d), (w.Skv * rs, rs, w.d, 1))
+        view.copy_(d[name])
+        kv.append(view)
+    R = m.relproj(d["r"], d["P"])
+    o, lse = m.attn_prefill(d["q"], kv[0], kv[1], R, window=w.window, return_lse=True)
+    torch.cuda.synchronize()
+    wo, wl = oracle_full(inp, w)
+    check("large-stride E100 o", o, wo, False)
+    check("large-stride E100 lse", lse, wl, True, extra_tol=2e-2)
+    wo0, _ = oracle.attention(inp["q"], inp["k"], inp["v"], None, window=w.window)
+    check_bias_seen("large-stride E100 bias", o, wo, wo0)
     del kv, buf
     torch.cuda.empty_cache()
 
@@ -302,9 +405,10 @@ def test_decode_split_invariance_and_prefill_agreement():
     for o, l in outs[1:]:
         assert torch.max(torch.abs(l - l1)).item() <= 1e-3
         assert torch.max(torch.abs(o.float() - o1.float())).item() <= 2.0 ** -7 * max(1.0, o1.float().abs().max().item())
-    # decode with Sq rows equals prefill of the same rows
+    # decode with Sq rows equals prefill of the same rows (o and lse)
     op, lp = run_path(inp, w, decode=False)
     assert torch.max(torch.abs(lp - l1)).item() <= 1e-3
+    assert torch.max(torch.abs(op.float() - o1.float())).item() <= 2.0 ** -7 * max(1.0, o1.float().abs().max().item())
 
 
 # --------------------------------------------------------------------------- combine kernel on its own
@@ -343,17 +447,35 @@ def test_one_hot_bias_exact(dstar, window, decode):
     """q = k = 0, R one-hot 30 at distance d*, v coded by position in two
     bf16-exact channels: o must decode exactly to key p - d* (or equal the
     plain mean when that key is not visible)."""
+    one_hot_case(2, 600, 9 if decode else 600, 64, 16, 2, dstar, window, decode)
+
+
+@pytest.mark.parametrize("dstar,window", [(0, 0), (1, 0), (99, 0), (37, 60), (70, 50)])
+def test_one_hot_bias_exact_unaligned_rows(dstar, window):
+    """As above through the two-group prefill kernel (G = 8) with an extent
+    of 100: bias rows not 16-byte aligned, staged by element loads."""
+    one_hot_case(1, 333, 333, 100, 16, 2, dstar, window, False)
+
+
+@pytest.mark.parametrize("dstar,window", [(0, 0), (1, 0), (511, 0), (300, 700), (64, 0)])
+def test_one_hot_bias_exact_persistent_rounds(dstar, window):
+    """The prefill workloads' heads and extent (Hq = 64, Hkv = 8, E = 512) at
+    1100 rows: 8 x 35 = 280 work items, more than the CUs and a multiple of 8,
+    so the persistent grid takes them in rounds with its XCD-aware order."""
+    one_hot_case(1, 1100, 1100, 512, 64, 8, dstar, window, False)
+
+
+def one_hot_case(B, S, Sq, E, Hq, Hkv, dstar, window, decode):
     m = rba()
-    S, E, Hq, Hkv = 600, 64, 16, 2
-    Sq = 9 if decode else S
-    q = torch.zeros(2, Sq, Hq, 128, dtype=torch.bfloat16)
-    k = torch.zeros(2, S, Hkv, 128, dtype=torch.bfloat16)
-    v = torch.zeros(2, S, Hkv, 128, dtype=torch.bfloat16)
+    say(f"one-hot B={B} S={S} Sq={Sq} E={E} Hq={Hq} Hkv={Hkv} d*={dstar} W={window} decode={decode}")
+    q = torch.zeros(B, Sq, Hq, 128, dtype=torch.bfloat16)
+    k = torch.zeros(B, S, Hkv, 128, dtype=torch.bfloat16)
+    v = torch.zeros(B, S, Hkv, 128, dtype=torch.bfloat16)
     j = torch.arange(S)
     v[:, :, :, 0] = (j % 256).to(torch.bfloat16)[None, :, None]
     v[:, :, :, 1] = (j // 256).to(torch.bfloat16)[None, :, None]
-    v[:, :, 1, 2] = 1.0
-    R = torch.zeros(2, Sq, Hq, E, dtype=torch.bfloat16)
+    v[:, :, Hkv - 1, 2] = 1.0
+    R = torch.zeros(B, Sq, Hq, E, dtype=torch.bfloat16)
     R[..., dstar] = 30.0
     d = {n: t.to(DEV) for n, t in dict(q=q, k=k, v=v, R=R).items()}
     if decode:

@@ -175,3 +175,35 @@ def test_prologue_mxfp8_cache():
         ok = (np.abs(dec - want) <= step * 0.51 + 2.0 ** -8 * np.abs(want)) | (np.abs(want) / sc > 448)
         say(f"[mxfp8 {name}] rows {len(bs)}, entries within a half step: {ok.mean():.6f}")
         assert ok.all(), f"{name}: {np.sum(~ok)} entries off"
+
+
+def test_prologue_ignores_garbage_state_before_sequence_start():
+    """Conv-state rows of positions before a sequence's start hold large
+    garbage here (the generator zeroes them; a serving engine need not): the
+    rows the call writes must not depend on them.  The oracle of the same
+    inputs treats those rows as zero, and the outputs must also equal those of
+    the zeroed state; the carried state is a plain copy either way."""
+    inp = make_prologue_inputs(MIX["new"], MIX["lens"], Hq=16, Hkv=2, W=4, seed=17)
+    clean_q, clean_k, clean_v, pos, _, _ = oracle_of(inp)
+    g = torch.Generator().manual_seed(99)
+    garbage = dict(inp)
+    garbage["state_k"] = inp["state_k"].clone()
+    garbage["state_v"] = inp["state_v"].clone()
+    n_garbage = 0
+    for b, (n, L) in enumerate(zip(MIX["new"], MIX["lens"])):
+        start = L - n
+        for j in range(3):
+            if start - 3 + j < 0:
+                garbage["state_k"][b, j] = (torch.randn(2, 128, generator=g) * 300).to(torch.bfloat16)
+                garbage["state_v"][b, j] = (torch.randn(2, 128, generator=g) * 300).to(torch.bfloat16)
+                n_garbage += 1
+    assert n_garbage >= 6          # the two sequences that start inside the call, and the 2-token one
+    qo, kc, vc, _, _, sk, sv = run(garbage, 512)
+    q_o, k_o, v_o, pos_g, nsk, nsv = oracle_of(garbage)
+    assert np.array_equal(pos, pos_g)
+    assert np.allclose(k_o, clean_k, rtol=0, atol=0) and np.allclose(v_o, clean_v, rtol=0, atol=0)
+    close("q_out", qo, clean_q)
+    bs = seq_of(inp)
+    close("k rows (garbage state)", kc[bs, pos], clean_k)
+    close("v rows (garbage state)", vc[bs, pos], clean_v)
+    assert np.array_equal(sk.double().cpu().numpy(), nsk) and np.array_equal(sv.double().cpu().numpy(), nsv)
