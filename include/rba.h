@@ -208,6 +208,21 @@ size_t rba_decode_workspace_bytes(const rba_attn_args *args, int num_splits);
 rba_status rba_attn_decode(const rba_attn_args *args, int num_splits, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/* rba_attn_decode without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the split partials go to a scratch array
+ * of RBA_DECODE_SCRATCH_BYTES that the library holds in device memory, one per
+ * device, for the life of the process.  The call itself allocates nothing.
+ * Same arguments, results and errors as rba_attn_decode; returns
+ * RBA_E_WORKSPACE before any launch when the partials of `num_splits` splits
+ * (rba_decode_workspace_bytes) exceed RBA_DECODE_SCRATCH_BYTES, and
+ * RBA_E_LAUNCH if the scratch array's address cannot be looked up.  Every
+ * call on one device shares that device's array (each call overwrites all of
+ * the part it reads): calls that overlap on one device, on different streams
+ * or from different threads without ordering, race.                        */
+#define RBA_DECODE_SCRATCH_BYTES (16u << 20)
+rba_status rba_attn_decode_noalloc(const rba_attn_args *args, int num_splits, void *stream);
+
 /* Paged, variable-length K/V for rba_attn_paged ([V-KV]).  The cache is a
  * pool of pages of page_size consecutive keys of every kv head:
  *   args->k, args->v : [num_pages][page_size][Hkv][d]  strides k_s / v_s =

@@ -19,7 +19,7 @@ import os
 import torch
 
 __all__ = [
-    "relproj", "attn_prefill", "attn_decode", "attn_paged", "splitkv_combine", "num_splits", "mxfp8_quantize",
+    "relproj", "attn_prefill", "attn_decode", "attn_decode_noalloc", "attn_paged", "splitkv_combine", "num_splits", "mxfp8_quantize",
     "attn_prologue", "cache_args",
     "decode_workspace_bytes", "lib_path", "RBAError",
     "RBA_OK", "RBA_E_INVALID", "RBA_E_UNSUPPORTED", "RBA_E_WORKSPACE", "RBA_E_LAUNCH",
@@ -30,6 +30,7 @@ lib_path = os.path.join(_HERE, "librba.so")
 
 RBA_OK, RBA_E_INVALID, RBA_E_UNSUPPORTED, RBA_E_WORKSPACE, RBA_E_LAUNCH = range(5)
 RBA_FP32, RBA_BF16 = 0, 1
+RBA_DECODE_SCRATCH_BYTES = 16 << 20     # size of the scratch array of rba_attn_decode_noalloc
 RBA_KV_PLAIN, RBA_KV_MXFP8 = 0, 1
 
 
@@ -121,6 +122,8 @@ def _load():
     lib.rba_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.rba_attn_decode.argtypes = [P, ci, vp, ctypes.c_size_t, vp]
     lib.rba_attn_decode.restype = ci
+    lib.rba_attn_decode_noalloc.argtypes = [P, ci, vp]
+    lib.rba_attn_decode_noalloc.restype = ci
     lib.rba_attn_paged.argtypes = [P, ctypes.POINTER(_PagedKV), ci, vp, ctypes.c_size_t, vp]
     lib.rba_attn_paged.restype = ci
     lib.rba_attn_prologue.argtypes = [ctypes.POINTER(_PrologueArgs), P, ctypes.POINTER(_PagedKV), vp]
@@ -362,6 +365,21 @@ def attn_decode(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0, nu
     code = _lib.rba_attn_decode(ctypes.byref(a), splits, ws_ptr, ws_bytes, _stream(q.device))
     _check("rba_attn_decode", code)
     return (o, lse) if return_lse else o
+
+
+def attn_decode_noalloc(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0, num_splits=0,
+                        out=None, lse=None, k_scale=None, v_scale=None):
+    """attn_decode with the split partials in the library's own device
+    scratch array (rba_attn_decode_noalloc): the C call allocates nothing.
+    Pass `out` (and `lse` [B, Hq, Sq] fp32, optional) to keep this wrapper
+    from allocating them.  Calls that overlap on one device race."""
+    _check_attn_inputs(q, k, v, R, k_scale, v_scale)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    a = make_args(q, k, v, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base,
+                  k_scale=k_scale, v_scale=v_scale)
+    code = _lib.rba_attn_decode_noalloc(ctypes.byref(a), int(num_splits), _stream(q.device))
+    _check("rba_attn_decode_noalloc", code)
+    return (o, lse) if lse is not None else o
 
 
 def make_paged(block_table, seq_lens, page_size: int, num_pages: int) -> _PagedKV:

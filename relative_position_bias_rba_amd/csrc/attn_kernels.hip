@@ -45,6 +45,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 namespace rba {
@@ -1654,6 +1655,33 @@ hipError_t launch_combine(const float *o_part, const float *lse_part, int splits
                                (float *)o, os0, os1, os2, lse);
     }
     return hipGetLastError();
+}
+
+// Split-KV workspace of rba_attn_decode_noalloc: a file-scope device array of
+// RBA_DECODE_SCRATCH_BYTES.  Every device the library runs on holds its own
+// copy until the process ends, and every call on that device shares it.  In
+// host code the name `scratch` is only a stand-in for the symbol, not a
+// device address: host code uses the address scratch_address() looks up once
+// per device (with that device current), never the name itself.
+static __device__ __align__(256) float scratch[RBA_DECODE_SCRATCH_BYTES / sizeof(float)];
+
+hipError_t scratch_address(void **out) {
+    static std::mutex mu;
+    static void *addr[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (ptr == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = ptr;
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace rba

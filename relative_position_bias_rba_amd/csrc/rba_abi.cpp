@@ -276,8 +276,10 @@ size_t rba_decode_workspace_bytes(const rba_attn_args *args, int num_splits) {
     return workspace_bytes(args, num_splits);
 }
 
-rba_status rba_attn_decode(const rba_attn_args *args, int num_splits, void *workspace, size_t workspace_bytes_,
-                           void *stream) {
+// Shared by rba_attn_decode and rba_attn_decode_noalloc.  scratch: take the
+// workspace from the library's device scratch array instead of the caller.
+static rba_status decode_impl(const rba_attn_args *args, int num_splits, void *workspace, size_t workspace_bytes_,
+                              bool scratch, void *stream) {
     const rba_status st = validate_attn(args);
     if (st != RBA_OK) return st;
     if (num_splits < 0 || num_splits > kMaxSplits) return RBA_E_INVALID;
@@ -294,6 +296,11 @@ rba_status rba_attn_decode(const rba_attn_args *args, int num_splits, void *work
         return rba::launch_attention(p, pl.var, s) == hipSuccess ? RBA_OK : RBA_E_LAUNCH;
     }
     const size_t need = workspace_bytes(args, num_splits);
+    if (scratch) {
+        if (need > RBA_DECODE_SCRATCH_BYTES) return RBA_E_WORKSPACE;
+        if (rba::scratch_address(&workspace) != hipSuccess) return RBA_E_LAUNCH;
+        workspace_bytes_ = RBA_DECODE_SCRATCH_BYTES;
+    }
     if (workspace == nullptr || workspace_bytes_ < need || !aligned(workspace, 16)) return RBA_E_WORKSPACE;
     rba::AttnParams p = make_params(args, pl, num_splits);
     const size_t rows = (size_t)args->B * args->Sq * args->Hq;
@@ -301,6 +308,15 @@ rba_status rba_attn_decode(const rba_attn_args *args, int num_splits, void *work
     p.lse_part = p.o_part + (size_t)num_splits * rows * kHeadDim;
     if (rba::launch_attention(p, pl.var, s) != hipSuccess) return RBA_E_LAUNCH;
     return rba_splitkv_combine(p.o_part, p.lse_part, num_splits, args, stream);
+}
+
+rba_status rba_attn_decode(const rba_attn_args *args, int num_splits, void *workspace, size_t workspace_bytes_,
+                           void *stream) {
+    return decode_impl(args, num_splits, workspace, workspace_bytes_, false, stream);
+}
+
+rba_status rba_attn_decode_noalloc(const rba_attn_args *args, int num_splits, void *stream) {
+    return decode_impl(args, num_splits, nullptr, 0, true, stream);
 }
 
 rba_status rba_attn_paged(const rba_attn_args *args, const rba_paged_kv *kv, int num_splits, void *workspace,

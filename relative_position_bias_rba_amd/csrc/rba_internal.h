@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rba.h"
+
 namespace rba {
 
 // One attention launch.  Query rows are grouped into blocks of QB consecutive
@@ -107,5 +109,9 @@ hipError_t launch_mxfp8_quantize(bool in_bf16, int64_t rows, int n, const void *
 hipError_t launch_calib_read(const void *buf, int64_t bytes, void *sink, int blocks, hipStream_t stream);
 
 hipError_t launch_calib_mfma(int iters, int blocks, void *sink, hipStream_t stream);
+
+// Device address of the library's split-KV scratch array on the current
+// device (looked up on the first call per device).
+hipError_t scratch_address(void **out);
 
 }  // namespace rba

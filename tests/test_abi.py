@@ -132,6 +132,21 @@ def test_decode_workspace_checks():
                                    ctypes.byref(a), None) == RBA_E_INVALID
 
 
+def test_decode_noalloc_host_checks():
+    """rba_attn_decode_noalloc rejects, before any launch, split partials
+    larger than its scratch array, and bad arguments as rba_attn_decode does."""
+    q, k, v, R, o = _tensors(B=64, Sq=9, Skv=640, Hq=64, Hkv=8)
+    a = make_args(q, k, v, R, o)
+    need = lib.rba_decode_workspace_bytes(ctypes.byref(a), 2)
+    assert need > rba.RBA_DECODE_SCRATCH_BYTES
+    assert lib.rba_attn_decode_noalloc(ctypes.byref(a), 2, None) == RBA_E_WORKSPACE
+    assert lib.rba_attn_decode_noalloc(ctypes.byref(a), -1, None) == RBA_E_INVALID
+    assert lib.rba_attn_decode_noalloc(ctypes.byref(a), 5000, None) == RBA_E_INVALID
+    a.Hq = 7                      # not a multiple of Hkv
+    assert lib.rba_attn_decode_noalloc(ctypes.byref(a), 2, None) == RBA_E_INVALID
+    assert lib.rba_attn_decode_noalloc(None, 2, None) == RBA_E_INVALID
+
+
 def _paged(B=2, Sq=3, ps=64, n_pages=10, Hq=8, Hkv=2, E=16, n_max=4):
     q = torch.zeros(B, Sq, Hq, 128, dtype=torch.bfloat16)
     kp = torch.zeros(n_pages, ps, Hkv, 128, dtype=torch.bfloat16)
