@@ -1,17 +1,25 @@
 """Benchmark of the relative-position-bias attention hot path on one MI355X.
 
-A step is one pass of the prefill hot path over the sliding-window prefill
-workload (B=1, S=8192, Hq=64, Hkv=8, d=128, r_dim=64, E=512, window 4096,
-bf16): the relative-logit projection R = r.P followed by the attention
-prefill, with all inputs resident in HBM.  `value` is attention TFLOP/s
-(4*d*Hq flops per visible query/key pair) over the whole step.  The same JSON
-line carries the kernel-level roofline of the dominant kernel (attention,
-timed with HIP events on the stream it runs on), the split-KV decode
-workloads' KV GB/s, the streaming-read bandwidth and MFMA rate the device
-attains (each rate is also given as a fraction of those), and the fp64 CPU
-oracle timed on a bounded sample.
+A step is one pass of the prefill hot path over the full-causal prefill
+workload (B=2, S=32768, Hq=64, Hkv=8, d=128, r_dim=64, E=512, log-scale base
+4096, bf16), the largest workload that runs on one GPU: the relative-logit
+projection R = r.P followed by the attention prefill, with all inputs resident
+in HBM.  `value` is attention TFLOP/s (4*d*Hq flops per visible query/key
+pair) over the whole step.  The same JSON line carries:
+  * `roofline`: the dominant kernel (attention) of that step, timed with HIP
+    events on the stream it runs on;
+  * `cpu_baseline`: the fp64 CPU oracle on a bounded row sample of the same
+    workload, its rate extrapolated to the whole workload;
+  * `workloads`: every other workload (the fp32 parity case, the sliding-window
+    prefill, the two decode halves, the long-context decode), each with its own
+    `roofline` object and its own oracle timing beside it;
+  * the paged, MXFP8, fused-projection and attention-prologue variants, the
+    streaming-read bandwidth and MFMA rate the device attains, and the device.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--legs a,b,...]
+
+--legs selects what runs (default: all): c1, c2, c3, c4w, c4f, c5, paged,
+mxfp8, prologue, attainable.  The headline step is c3.
 """
 from __future__ import annotations
 
@@ -27,16 +35,24 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3      # dense fp32 MFMA
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# HBM bytes per launch of the prefill kernel: rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors
-# from a plain 1 GiB device copy under the same counters), keyed by the sha256 prefix of the kernel
-# source the counters were taken on; any other source reports null.
-PROFILED_TRAFFIC = {"7013f822c18c012b": 508731 * 1024 * 2 + 131590 * 1024}
+# HBM bytes per launch of each leg's dominant kernel: rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
+# (factors from a plain 1 GiB device copy under the same counters), keyed by leg and by the sha256
+# prefix of the kernel source the counters were taken on; any other source reports null.
+PROFILED_TRAFFIC = {
+    ("c2", "7013f822c18c012b"): 508731 * 1024 * 2 + 131590 * 1024,
+    ("c3", "7013f822c18c012b"): 6513701 * 1024 * 2 + 1049089 * 1024,
+}
+
+
+def traffic(leg):
+    return PROFILED_TRAFFIC.get((leg, kernel_source_hash()))
 
 
 def kernel_source_hash():
@@ -111,49 +127,91 @@ def c_launcher(rba, name, *args):
     return lambda: fn(*args)
 
 
-def cpu_baseline(w, inp, budget_s=15.0):
-    """The fp64 oracle on a sample of query rows of the workload (all heads)."""
+def cpu_threads():
+    """(threads the oracle's BLAS uses, cores in this process's affinity mask)."""
+    aff = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
+    except Exception:  # pragma: no cover
+        blas = aff
+    return blas, aff
+
+
+def cpu_baseline(w, inp, budget_s, *, fixed=(), seed=7, batch=8, sample_note=""):
+    """The fp64 oracle (test infrastructure, timed as it stands) on query rows of
+    workload w (all heads): the `fixed` rows first, then seeded random rows, in
+    batches, until budget_s of oracle time is spent.  Prefill reports TFLOP/s of
+    visible query/key pairs, decode (Sq <= 32, every row of a sequence at once)
+    KV GB/s-equivalent over the sequences it covered; both are extrapolated to
+    the whole workload as `extrapolated_s`."""
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    rng = np.random.default_rng(7)
-    rows_all = [(0, int(t)) for t in rng.permutation(w.Sq)]
+    decode = w.Sq <= 32
+    rng = np.random.default_rng(seed)
+    if decode:
+        seqs = [int(b) for b in rng.permutation(w.B)]
+        units = [[(b, t) for t in range(w.Sq)] for b in seqs]
+    else:
+        rows = [(b, t) for b in range(w.B) for t in fixed if t < w.Sq]
+        seen = set(rows)
+        for i in rng.permutation(w.B * w.Sq)[:4096]:
+            r = (int(i) // w.Sq, int(i) % w.Sq)
+            if r not in seen:
+                rows.append(r)
+                seen.add(r)
+        units = [rows[i:i + batch] for i in range(0, len(rows), batch)]
 
     def R_row(b, t):
         return oracle.relproj(inp["r"][b, t], inp["P"])
 
-    done, flops, t_used = 0, 0.0, 0.0
-    batch = 8
-    while t_used < budget_s and done < len(rows_all):
-        rows = rows_all[done:done + batch]
+    done_rows, work, t_used, n_units = 0, 0.0, 0.0, 0
+    for u in units:
+        if t_used >= budget_s:
+            break
         t0 = time.perf_counter()
-        oracle.attention_rows(inp["q"], inp["k"], inp["v"], R_row, rows, window=w.window,
+        oracle.attention_rows(inp["q"], inp["k"], inp["v"], R_row, u, window=w.window,
                               log_scale_base=w.log_scale_base)
         t_used += time.perf_counter() - t0
-        for _, t in rows:
-            p = w.Skv - w.Sq + t
-            lo = 0 if w.window == 0 else max(0, p - w.window + 1)
-            flops += 4.0 * w.d * w.Hq * (p - lo + 1)
-        done += len(rows)
-    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} query rows x {w.Hq} heads of {w.name} (fp64 NumPy, R rows recomputed "
-                      f"from r and P), {t_used:.1f} s"}
+        n_units += 1
+        done_rows += len(u)
+        if decode:
+            p_lo, p_hi = w.Skv - w.Sq, w.Skv - 1
+            lo = 0 if w.window == 0 else max(0, p_lo - w.window + 1)
+            work += (p_hi - lo + 1) * w.Hkv * w.d * 2 * (4 if w.dtype == "fp32" else 2)
+        else:
+            for _, t in u:
+                p = w.Skv - w.Sq + t
+                lo = 0 if w.window == 0 else max(0, p - w.window + 1)
+                work += 4.0 * w.d * w.Hq * (p - lo + 1)
+    blas, aff = cpu_threads()
+    if decode:
+        value, unit, total = work / t_used / 1e9, "GB/s", w.kv_bytes()
+        what = f"{n_units} of {w.B} sequences (all {w.Sq} rows, {w.Hq} heads)"
+    else:
+        value, unit, total = work / t_used / 1e12, "TFLOP/s", w.attn_flops()
+        what = f"{done_rows} of {w.B * w.Sq} query rows x {w.Hq} heads"
+    full = n_units == len(units)
+    return {"value": round(value, 6), "unit": unit, "cores": int(blas), "affinity_cores": int(aff),
+            "blas_threads": int(blas), "kind": "oracle",
+            "sample": f"{what} of {w.name} (fp64 NumPy, R rows recomputed from r and P), {t_used:.1f} s"
+                      + (f"; {sample_note}" if sample_note else ""),
+            "oracle_s": round(t_used, 2),
+            ("measured_s" if full else "extrapolated_s"): round(t_used if full else total / (work / t_used), 1)}
 
 
-def decode_leg(rba, torch, name, reps, mxfp8=False):
+def decode_leg(rba, torch, name, reps, mxfp8=False, leg=None, cpu_budget=0.0):
     """One decode workload; mxfp8: its K/V cache encoded to MXFP8 by the library's
-    encoder (timed too) and attention run over the encoded cache."""
+    encoder (timed too) and attention run over the encoded cache.  With
+    cpu_budget > 0 the oracle is timed on a sample of the same inputs."""
     from workloads import CONFIGS, make_inputs
     w = CONFIGS[name]
     log(f"decode {name}{' mxfp8' if mxfp8 else ''}: generating inputs")
     inp = make_inputs(w)
     d = {k: v.to("cuda") for k, v in inp.items()}
-    del inp
+    if cpu_budget <= 0:
+        del inp
     R = rba.relproj(d["r"], d["P"])
     splits = rba.num_splits(d["q"], d["k"], d["v"], R, window=w.window)
     o = torch.empty_like(d["q"])
@@ -189,14 +247,22 @@ def decode_leg(rba, torch, name, reps, mxfp8=False):
     ms_warm = time_launches(launch, reps, torch)
     ms = time_cold(launch, max(reps, 50), torch)
     gbs = kv_bytes / (ms * 1e-3) / 1e9
+    kname = "attn_fwd_kernel<bf16, 4 waves" + (", MXFP8>" if mxfp8 else ">") + (" + combine_kernel" if splits > 1 else "")
     res = {"ms": round(ms, 4), "kv_GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
            "ms_warm": round(ms_warm, 4), "num_splits": splits, "kv_bytes": kv_bytes,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic(leg) if leg else None,
+                        "kernel": kname, "avg_ms": round(ms, 4), "algorithmic_bytes": kv_bytes},
            "timing": "median of 50 launches, each after a 512 MiB read that evicts the caches; ms_warm: back-to-back mean"}
     if mxfp8:
         res["kv_format"] = "MXFP8 (E4M3 codes + E8M0 scale per 32 head-dim entries)"
     res.update(extra)
     del d, R, o, ws, keep
     torch.cuda.empty_cache()
+    if cpu_budget > 0:
+        log(f"decode {name}: oracle on a sample ...")
+        res["cpu_baseline"] = cpu_baseline(w, inp, cpu_budget)
+        res["gpu_over_cpu"] = round(gbs / res["cpu_baseline"]["value"], 1)
     return res
 
 
@@ -283,40 +349,112 @@ def prologue_leg(rba, torch, name, new_tokens, seq_lens, Skv, reps, mxfp8=False)
     return res
 
 
-def full_prefill_leg(rba, torch, reps=5):
-    """Full-causal prefill with the length-dependent log scale (B=2, S=32768, 64/8
-    heads, E=512): relproj + attention, and the attention kernel alone."""
+def prefill_leg(rba, torch, name, leg, steps, warmup, cpu_budget, fixed_rows=()):
+    """One prefill workload: the step (relproj + attention through the binding)
+    timed over `steps` steps after warm-up; the attention kernel and the
+    projection alone (C ABI, prebuilt arguments, back to back); the fused
+    kernel (projection computed inside the prefill); the oracle on a sample."""
     from workloads import CONFIGS, make_inputs
-    w = CONFIGS["c3_full_prefill"]
-    log("full prefill: generating inputs")
+    w = CONFIGS[name]
+    log(f"prefill {name}: generating inputs {w}")
     inp = make_inputs(w)
     d = {k: v.to("cuda") for k, v in inp.items()}
-    del inp
-    R = rba.relproj(d["r"], d["P"])
     o = torch.empty_like(d["q"])
-    a = rba.make_args(d["q"], d["k"], d["v"], R, o, None, window=w.window, log_scale_base=w.log_scale_base)
-    ms = time_launches(c_launcher(rba, "rba_attn_prefill", ctypes.byref(a), rba._stream(o.device)), reps, torch)
+    dev = d["q"].device
+
+    def step():
+        Rn = rba.relproj(d["r"], d["P"])
+        rba.attn_prefill(d["q"], d["k"], d["v"], Rn, window=w.window, log_scale_base=w.log_scale_base, out=o)
+        return Rn
+
+    # W warm-up steps, then more untimed steps until ~100 ms have passed so that
+    # the clocks have left their idle state before the timed steps
+    t_w = time.perf_counter()
+    warm_run = 0
+    while warm_run < warmup or (time.perf_counter() - t_w) < 0.1:
+        R = step()
+        warm_run += 1
+        if warm_run % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        R = step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+
+    reps = max(steps, 10) if w.Sq * w.B <= 16384 else max(steps // 2, 5)
+    a_attn = rba.make_args(d["q"], d["k"], d["v"], R, o, None, window=w.window, log_scale_base=w.log_scale_base)
+    ms_attn = time_launches(c_launcher(rba, "rba_attn_prefill", ctypes.byref(a_attn), rba._stream(dev)), reps, torch)
     r2 = d["r"].reshape(-1, w.r_dim)
     ms_rp = time_launches(c_launcher(rba, "rba_relproj", 1, 1, r2.shape[0], w.Hq, w.r_dim, w.E,
                                      ctypes.c_void_p(r2.data_ptr()), r2.stride(0), 0,
                                      ctypes.c_void_p(d["P"].data_ptr()), ctypes.c_void_p(R.data_ptr()),
-                                     rba._stream(o.device)), reps, torch)
-    # the same step with the projection computed inside the prefill kernel
-    PT = rba.relproj_pack(d["P"])
-    af = rba.make_args(d["q"], d["k"], d["v"], None, o, None, window=w.window, log_scale_base=w.log_scale_base)
-    af.E = w.E
-    rb = rba.make_relbias(d["r"], PT)
-    need = rba._lib.rba_prefill_fused_workspace_bytes(ctypes.byref(af))
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    ms_f = time_launches(c_launcher(rba, "rba_attn_prefill_fused", ctypes.byref(af), ctypes.byref(rb),
-                                    ctypes.c_void_p(ws.data_ptr()), need, rba._stream(o.device)), reps, torch)
+                                     rba._stream(dev)), reps, torch)
     flops = w.attn_flops()
-    res = {"attn_ms": round(ms, 3), "attn_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-           "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-           "relproj_ms": round(ms_rp, 3), "step_tflops": round(flops / ((ms + ms_rp) * 1e-3) / 1e12, 1),
-           "fused_ms": round(ms_f, 3), "fused_step_tflops": round(flops / (ms_f * 1e-3) / 1e12, 1),
-           "algorithmic_flops": flops, "timing": "back-to-back mean after a clock warm-up"}
-    del d, R, o, ws, PT
+    tf = flops / (ms_attn * 1e-3) / 1e12
+    rp_bytes = w.B * w.Sq * w.Hq * w.E * 2 + w.B * w.Sq * w.r_dim * 2 + w.Hq * w.r_dim * w.E * 2
+    res = {"workload": w.name, "step_ms": round(ms_step, 4),
+           "step_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2), "steps": steps, "warmup_steps_run": warm_run,
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic(leg),
+                        "kernel": "attn_prefill_pp_kernel<0>", "avg_ms": round(ms_attn, 4),
+                        "algorithmic_flops": flops},
+           "relproj": {"ms": round(ms_rp, 4), "GBps": round(rp_bytes / (ms_rp * 1e-3) / 1e9, 1),
+                       "frac_hbm": round(rp_bytes / (ms_rp * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "algorithmic_bytes": rp_bytes, "flops": w.relproj_flops()},
+           "timing": "step: wall clock over the timed steps after torch.cuda.synchronize; kernels: back-to-back "
+                     "mean of C-ABI launches between HIP events after a clock warm-up"}
+    del R
+    res["fused"] = fused_prefill_leg(rba, torch, w, d, reps, ms_attn + ms_rp)
+    del d, o, a_attn
+    torch.cuda.empty_cache()
+    if cpu_budget > 0:
+        log(f"prefill {name}: oracle on a row sample ...")
+        res["cpu_baseline"] = cpu_baseline(w, inp, cpu_budget, fixed=fixed_rows,
+                                           sample_note="fixed rows first, then seeded random rows" if fixed_rows else "")
+        res["gpu_over_cpu"] = round(tf / res["cpu_baseline"]["value"], 1)
+    return res
+
+
+def tiny_leg(rba, torch, cpu_budget):
+    """The fp32 parity workload (B=1, S=256, Hq=4, Hkv=1, E=64): the GPU result
+    against the oracle, the kernels' times and the oracle's time on all of it."""
+    import numpy as np
+
+    import oracle
+    from workloads import CONFIGS, make_inputs
+    w = CONFIGS["c1_tiny_fp32"]
+    inp = make_inputs(w)
+    d = {k: v.to("cuda") for k, v in inp.items()}
+    R = rba.relproj(d["r"], d["P"])
+    o, lse = rba.attn_prefill(d["q"], d["k"], d["v"], R, window=w.window, log_scale_base=w.log_scale_base,
+                              return_lse=True)
+    torch.cuda.synchronize()
+    dev = d["q"].device
+    a = rba.make_args(d["q"], d["k"], d["v"], R, o, None, window=w.window, log_scale_base=w.log_scale_base)
+    ms = time_launches(c_launcher(rba, "rba_attn_prefill", ctypes.byref(a), rba._stream(dev)), 50, torch)
+    flops = w.attn_flops()
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {"workload": w.name,
+           "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_FP32_TFLOPS, 5), "traffic": None,
+                        "kernel": "attn_fwd_kernel<float, 4 waves> (fp32 MFMA)", "avg_ms": round(ms, 4),
+                        "algorithmic_flops": flops},
+           "note": "parity case: 4 workgroups, far too small to fill the chip"}
+    if cpu_budget > 0:
+        t0 = time.perf_counter()
+        wo, wl = oracle.attention(inp["q"], inp["k"], inp["v"], oracle.relproj(inp["r"], inp["P"]), window=w.window,
+                                  log_scale_base=w.log_scale_base)
+        t = time.perf_counter() - t0
+        blas, aff = cpu_threads()
+        res["cpu_baseline"] = {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas),
+                               "affinity_cores": int(aff), "blas_threads": int(blas), "kind": "oracle",
+                               "sample": f"the whole workload (fp64 NumPy), {t:.2f} s", "oracle_s": round(t, 3),
+                               "measured_s": round(t, 3)}
+        res["parity_max_abs"] = {"o": float(np.abs(o.double().cpu().numpy() - wo).max()),
+                                 "lse": float(np.abs(lse.double().cpu().numpy() - wl).max()), "bound": 1e-5}
+    del d, R, o, lse
     torch.cuda.empty_cache()
     return res
 
@@ -366,132 +504,93 @@ def attainable(rba, torch):
                    "(back-to-back bf16 32x32x16 MFMA, 32 waves per CU), HIP events, after a clock warm-up"}
 
 
+ALL_LEGS = ("c1", "c2", "c3", "c4w", "c4f", "c5", "paged", "mxfp8", "prologue", "attainable")
+C3_FIXED_ROWS = (0, 1, 511, 512, 4095, 4096, 32767)     # extent and log-scale edges, the last row
+C2_FIXED_ROWS = (0, 1, 511, 512, 4095, 4096, 8191)      # extent and window edges, the last row
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--legs", default=",".join(ALL_LEGS),
+                    help="comma-separated subset of " + ",".join(ALL_LEGS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time per timed workload (the headline's and each other's)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
               f"(every box has one GPU and the path needs no collective).", file=sys.stderr)
         sys.exit(2)
+    legs = [x for x in args.legs.split(",") if x]
+    bad = [x for x in legs if x not in ALL_LEGS]
+    if bad:
+        print(f"unknown legs {bad}; choose from {ALL_LEGS}", file=sys.stderr)
+        sys.exit(2)
+    budget = 0.0 if args.no_cpu_baseline else args.cpu_budget
 
     import torch
 
     import relative_position_bias_rba_amd as rba
-    from workloads import CONFIGS, make_inputs
+    from workloads import CONFIGS
 
-    w = CONFIGS["c2_swa_prefill"]
-    log(f"prefill workload {w}")
-    inp = make_inputs(w)
-    d = {k: v.to("cuda") for k, v in inp.items()}
-    R = torch.empty(w.B, w.Sq, w.Hq, w.E, dtype=torch.bfloat16, device="cuda")
-    o = torch.empty_like(d["q"])
-
-    def step():
-        Rn = rba.relproj(d["r"], d["P"])
-        rba.attn_prefill(d["q"], d["k"], d["v"], Rn, window=w.window, log_scale_base=w.log_scale_base, out=o)
-        return Rn
-
-    # W warm-up steps, then more untimed steps until ~100 ms have passed so that
-    # the clocks have left their idle state before the timed steps
-    t_w = time.perf_counter()
-    warm_run = 0
-    while warm_run < args.warmup or (time.perf_counter() - t_w) < 0.1:
-        R = step()
-        warm_run += 1
-        if warm_run % 8 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-
-    # whole-step timing
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        R = step()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # kernel-level timing: back-to-back launches through the C ABI with prebuilt arguments,
-    # bracketed by HIP events on the stream the kernels run on
-    dev = d["q"].device
-    a_attn = rba.make_args(d["q"], d["k"], d["v"], R, o, None, window=w.window, log_scale_base=w.log_scale_base)
-    ms_attn = time_launches(c_launcher(rba, "rba_attn_prefill", ctypes.byref(a_attn), rba._stream(dev)),
-                            max(args.steps, 10), torch)
-    r2 = d["r"].reshape(-1, w.r_dim)
-    ms_relproj = time_launches(c_launcher(rba, "rba_relproj", 1, 1, r2.shape[0], w.Hq, w.r_dim, w.E,
-                                          ctypes.c_void_p(r2.data_ptr()), r2.stride(0), 0,
-                                          ctypes.c_void_p(d["P"].data_ptr()), ctypes.c_void_p(R.data_ptr()),
-                                          rba._stream(dev)),
-                               max(args.steps, 10), torch)
-
-    flops = w.attn_flops()
-    value = flops / (ms_step * 1e-3) / 1e12
-    attn_tflops = flops / (ms_attn * 1e-3) / 1e12
-    relproj_bytes = w.B * w.Sq * w.Hq * w.E * 2 + w.B * w.Sq * w.r_dim * 2 + w.Hq * w.r_dim * w.E * 2
-    out = {
-        "metric": "rel-bias attn prefill TFLOP/s & decode KV GB/s (% of MI355X roofline)",
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "warmup_steps_run": warm_run,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded normals)",
-        "config": {"workload": "sliding-window prefill B=1 S=8192 Hq=64 Hkv=8 d=128 r_dim=64 E=512 W=4096 "
-                               "(relproj + attention per step)",
-                   "global_batch": w.B, "seq_len": w.Sq, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": PROFILED_TRAFFIC.get(kernel_source_hash()),
-                     "kernel": "attn_prefill_pp_kernel<0>", "avg_ms": round(ms_attn, 4),
-                     "algorithmic_flops": flops},
-        "kernels": {"attn_prefill_ms": round(ms_attn, 4), "attn_prefill_tflops": round(attn_tflops, 2),
-                    "relproj_ms": round(ms_relproj, 4),
-                    "relproj_GBps": round(relproj_bytes / (ms_relproj * 1e-3) / 1e9, 1),
-                    "relproj_frac_hbm": round(relproj_bytes / (ms_relproj * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-    }
-    out["prefill_fused"] = fused_prefill_leg(rba, torch, w, d, max(args.steps, 10), ms_attn + ms_relproj)
-    del R, o
-    d_cpu = inp
-    del d
-    torch.cuda.empty_cache()
-
-    if not args.no_decode:
-        out["decode"] = {}
-        for name in ("c4_decode_swa", "c4_decode_full", "c5_long_decode"):
-            out["decode"][name] = decode_leg(rba, torch, name, 20)
-        out["decode"]["c4_decode_full_paged64"] = paged_decode_leg(rba, torch, "c4_decode_full", 64, 20, 8192)
+    out = {"metric": "rel-bias attn prefill TFLOP/s & decode KV GB/s (% of MI355X roofline)"}
+    work = {}
+    if "c3" in legs:
+        head = prefill_leg(rba, torch, "c3_full_prefill", "c3", args.steps, args.warmup, budget, C3_FIXED_ROWS)
+        w = CONFIGS["c3_full_prefill"]
+        value = w.attn_flops() / (head["step_ms"] * 1e-3) / 1e12
+        out.update({
+            "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "warmup_steps_run": head["warmup_steps_run"], "ms_per_step": head["step_ms"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded normals)",
+            "config": {"workload": "full-causal prefill B=2 S=32768 Hq=64 Hkv=8 d=128 r_dim=64 E=512, log-scale "
+                                   "base 4096 (relproj + attention per step)",
+                       "global_batch": w.B, "seq_len": w.Sq, "parallelism": "single GPU"},
+            "roofline": head["roofline"],
+            "cpu_baseline": head.get("cpu_baseline"),
+        })
+        work["c3_full_prefill"] = head
+    if "c2" in legs:
+        work["c2_swa_prefill"] = prefill_leg(rba, torch, "c2_swa_prefill", "c2", args.steps, args.warmup, budget,
+                                             C2_FIXED_ROWS)
+    if "c1" in legs:
+        work["c1_tiny_fp32"] = tiny_leg(rba, torch, budget)
+    for leg, name in (("c4w", "c4_decode_swa"), ("c4f", "c4_decode_full"), ("c5", "c5_long_decode")):
+        if leg in legs:
+            work[name] = decode_leg(rba, torch, name, 20, leg=leg, cpu_budget=budget)
+    out["workloads"] = work
+    extra = {}
+    if "paged" in legs:
+        extra["c4_decode_full_paged64"] = paged_decode_leg(rba, torch, "c4_decode_full", 64, 20, 8192)
+        extra["c4_decode_full_paged64"]["cpu_baseline_ref"] = "workloads.c4_decode_full (same oracle and shapes)"
+    if "mxfp8" in legs:
         for name in ("c4_decode_full", "c5_long_decode"):
-            out["decode"][name + "_mxfp8"] = decode_leg(rba, torch, name, 20, mxfp8=True)
-    if not args.no_decode:
-        out["prefill_full_causal"] = full_prefill_leg(rba, torch)
-    log("attention prologue ...")
-    out["prologue"] = {
-        "prefill_8192": prologue_leg(rba, torch, "prefill", [8192], [8192], 8192, 20),
-        "decode_64x9": prologue_leg(rba, torch, "decode", [9] * 64, [9216] * 64, 9216, 50),
-        "decode_64x9_mxfp8": prologue_leg(rba, torch, "decode", [9] * 64, [9216] * 64, 9216, 50, mxfp8=True),
-    }
-    att = attainable(rba, torch)
-    out["attainable"] = att
-    out["roofline"]["frac_attainable"] = round(out["roofline"]["achieved"] / att["mfma_bf16_TFLOPs"], 4)
-    for leg in out.get("decode", {}).values():
-        leg["frac_attainable"] = round(leg["kv_GBps"] / att["hbm_read_GBps"], 4)
+            extra[name + "_mxfp8"] = decode_leg(rba, torch, name, 20, mxfp8=True)
+            extra[name + "_mxfp8"]["cpu_baseline_ref"] = f"workloads.{name} (the oracle runs on the decoded cache)"
+    if extra:
+        out["decode_variants"] = extra
+    if "prologue" in legs:
+        log("attention prologue ...")
+        out["prologue"] = {
+            "prefill_8192": prologue_leg(rba, torch, "prefill", [8192], [8192], 8192, 20),
+            "decode_64x9": prologue_leg(rba, torch, "decode", [9] * 64, [9216] * 64, 9216, 50),
+            "decode_64x9_mxfp8": prologue_leg(rba, torch, "decode", [9] * 64, [9216] * 64, 9216, 50, mxfp8=True),
+        }
+    if "attainable" in legs:
+        att = attainable(rba, torch)
+        out["attainable"] = att
+        for wl in work.values():
+            rf = wl.get("roofline")
+            if rf and rf["unit"] == "TFLOP/s" and rf["peak"] == PEAK_BF16_TFLOPS:
+                rf["frac_attainable"] = round(rf["achieved"] / att["mfma_bf16_TFLOPs"], 4)
+            elif rf and rf["unit"] == "GB/s":
+                rf["frac_attainable"] = round(rf["achieved"] / att["hbm_read_GBps"], 4)
     out["device"] = {"name": torch.cuda.get_device_name(0), "hip": torch.version.hip,
                      "compute_units": torch.cuda.get_device_properties(0).multi_processor_count}
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) ...")
-        out["cpu_baseline"] = cpu_baseline(w, d_cpu, args.cpu_budget)
-    else:
-        out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
 
 
