@@ -64,6 +64,7 @@ constexpr int NT = 256;               // threads per workgroup of the combine ke
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;  // log2 growth of the running max tolerated before O is rescaled
+constexpr float kRescaleLimit = 256.f;   // 2^kRescaleSlack
 
 template <typename T>
 struct Tile;
@@ -1332,39 +1333,58 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-#pragma unroll
-        for (int u = 0; u < KT; ++u)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, S[u][r]);
         burst(6, 11);
-        mt *= amul;
-        mt = max_across_halves(mt);
-        // The reference max only moves when the tile max exceeds it by more
-        // than kRescaleSlack (alpha = 1 otherwise).
-        const bool grow = mt > m + kRescaleSlack;
-        const float mn = grow ? mt : m;
-        const float alpha = m == -INFINITY ? 0.f : (grow ? fast_exp2(m - mn) : 1.f);
-        m = mn;
-        l *= alpha;
-        o_scale = alpha;        // applied to O at the start of the next matrix phase
-        const float mu = m == -INFINITY ? 0.f : m;
+        // Probabilities against the current reference max m (exp2 domain);
+        // row sums over the same bf16 values the PV product uses.
         const float sa = amul;
         float sum = 0.f;
+        auto exps = [&](float mu, auto dma_b) __attribute__((always_inline)) {
+            constexpr bool DB = decltype(dma_b)::value;
+            float sm[2] = {0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < KT; ++u)
+            for (int u = 0; u < KT; ++u)
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                bf16x8 pb;
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    bf16x8 pb;
 #pragma unroll
-                for (int x = 0; x < 8; ++x) pb[x] = (__bf16)fast_exp2(fmaf(S[u][8 * h2 + x], sa, -mu));
+                    for (int x = 0; x < 8; ++x) pb[x] = (__bf16)fast_exp2(fmaf(S[u][8 * h2 + x], sa, -mu));
 #pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    sum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[2 * x], pb[2 * x + 1]},
-                                                          bf16x2{(__bf16)1.f, (__bf16)1.f}, sum, false);
-                P[2 * u + h2] = pb;
-                if (u == 0 && h2 == 0) burst(11, 15);
-                if (u == 0 && h2 == 1) burst(15, NSLOT);
-            }
+                    for (int x = 0; x < 4; ++x)
+                        sm[x & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[2 * x], pb[2 * x + 1]},
+                                                              bf16x2{(__bf16)1.f, (__bf16)1.f}, sm[x & 1], false);
+                    P[2 * u + h2] = pb;
+                    if constexpr (DB) {
+                        if (u == 0 && h2 == 0) burst(11, 15);
+                        if (u == 0 && h2 == 1) burst(15, NSLOT);
+                    }
+                }
+            sum = sm[0] + sm[1];
+        };
+        exps(m == -INFINITY ? 0.f : m, std::integral_constant<bool, DMA>{});
+        o_scale = 1.f;
+        // The reference max m only moves when the tile max exceeds it by more
+        // than kRescaleSlack.  While the lane's probabilities sum to at most
+        // 2^kRescaleSlack none of them exceeds that bound, so the tile max is
+        // not needed (an overflow makes the sum inf, a NaN fails the test);
+        // otherwise, and at a column's first visible tile, it is taken as
+        // before and, if m moves, O and l are rescaled and P recomputed.
+        // Wave-uniform, so both halves of a column decide alike.
+        const bool slow = !(sum <= kRescaleLimit) || m == -INFINITY;
+        if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+#pragma unroll
+            for (int u = 0; u < KT; ++u)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, S[u][r]);
+            mt *= amul;
+            mt = max_across_halves(mt);
+            const bool grow = mt > m + kRescaleSlack;
+            const float mn = grow ? mt : m;
+            const float alpha = m == -INFINITY ? 0.f : (grow ? fast_exp2(m - mn) : 1.f);
+            m = mn;
+            l *= alpha;
+            o_scale = alpha;        // applied to O at the start of the next matrix phase
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) exps(m == -INFINITY ? 0.f : m, std::false_type{});
+        }
         l += sum;
     };
 
