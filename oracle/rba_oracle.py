@@ -61,6 +61,11 @@ design notes):
     x / 2^e rounded to the nearest E4M3 value, ties to even, saturated to
     +-448.  K and V are blocked along the head dimension (32 entries), and
     attention with an MXFP8 cache is the attention over the decoded values.
+  * MXFP8 logits ([S-FA4]: the attention kernel itself runs in MXFP8; [V-FP8]
+    names FP8 attention against compute limits): in that mode q is encoded
+    the same way (blocks of 32 along the head dimension, the same rule) and
+    the logits are the dot products of the decoded q and the decoded K; the
+    probabilities and V stay as in the plain MXFP8-cache reading.
   * Attention prologue ([S-SC]): ShortConv tap i multiplies the row i
     positions back (tap 0 = the current token), no bias, no activation;
     positions before a sequence's start read zero.  RMSNorm is
@@ -104,6 +109,7 @@ __all__ = [
     "attention_prologue",
     "mxfp8_quantize",
     "mxfp8_dequantize",
+    "attention_mxfp8_logits",
 ]
 
 
@@ -451,6 +457,20 @@ def mxfp8_dequantize(codes, scales):
     vals = e4m3_value(codes).reshape(*codes.shape[:-1], n // MX_BLOCK, MX_BLOCK)
     s = np.where(scales == 255, np.nan, np.ldexp(1.0, scales - 127))
     return (vals * s[..., None]).reshape(codes.shape)
+
+
+def attention_mxfp8_logits(q, k_codes, k_scales, v_codes, v_scales, R=None, *, window=0, scale=None,
+                           log_scale_base=0.0, chunk=512):
+    """Attention whose logits are computed in MXFP8 ([S-FA4]): q is encoded
+    with mxfp8_quantize (blocks of 32 along the head dimension), K and V are
+    an MXFP8 cache (codes [B, Skv, Hkv, d], scales [B, Skv, Hkv, d/32]); the
+    logit of (query, key) is scale * <decoded q, decoded k> (+ bias, log
+    scale as in attention), and the output weights the decoded V.  Returns
+    o, lse as attention does."""
+    qc, qs = mxfp8_quantize(q)
+    return attention(mxfp8_dequantize(qc, qs), mxfp8_dequantize(k_codes, k_scales),
+                     mxfp8_dequantize(v_codes, v_scales), R, window=window, scale=scale,
+                     log_scale_base=log_scale_base, chunk=chunk)
 
 
 # --------------------------------------------------------------------------- attention prologue ([S-SC])

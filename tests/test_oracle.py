@@ -619,3 +619,59 @@ def test_prologue_composition_closed_forms():
     assert np.allclose(v_rows[0, 0], (1.0 + c) * w, rtol=0, atol=1e-13)
     assert np.allclose(q_out[0], np.broadcast_to(gq, (Hq, d)), rtol=0, atol=1e-14)
     assert list(pos) == [9]
+
+
+# --------------------------------------------------------------------------- MXFP8 logits
+
+def test_mxfp8_logits_closed_form_quantizes_q():
+    """One query, two keys, hand-worked.  q's first block is (1.1, 0, ...): its
+    shared exponent is floor(log2 1.1) - 8 = -8 and 1.1 * 2^8 = 281.6 rounds
+    to the E4M3 value 288, so the decoded entry is 1.125.  k0 = e_0 (exact in
+    E4M3), k1 = 0, v0 = e_0, v1 = e_1: o = (sigmoid(x), 1 - sigmoid(x), 0, ...)
+    with x = 1.125 / sqrt(128), and lse = ln(e^x + 1).  Unquantized q (1.1)
+    would give a different o, so the pin tells an encoded q from a raw one.
+    A second head whose q is 1e5 in its first entry checks that blocks stay
+    within a head's 128 entries: sharing a block with it would give head 0
+    the exponent 16 - 8 = 8, and 1.1 / 2^8 would round to the subnormal
+    2 * 2^-9, i.e. a decoded 1.0 instead of 1.125."""
+    from oracle import attention_mxfp8_logits, mxfp8_quantize
+    d = 128
+    q = np.zeros((1, 1, 2, d))
+    q[0, 0, 0, 0] = 1.1
+    q[0, 0, 1, 0] = 1e5
+    k = np.zeros((1, 2, 1, d))
+    k[0, 0, 0, 0] = 1.0
+    v = np.zeros((1, 2, 1, d))
+    v[0, 0, 0, 0] = 1.0
+    v[0, 1, 0, 1] = 1.0
+    kc, ks = mxfp8_quantize(k)
+    vc, vs = mxfp8_quantize(v)
+    o, lse = attention_mxfp8_logits(q, kc, ks, vc, vs)
+    x = 1.125 / math.sqrt(d)
+    w0 = 1.0 / (1.0 + math.exp(-x))
+    assert abs(o[0, 0, 0, 0] - w0) <= 1e-12 and abs(o[0, 0, 0, 1] - (1.0 - w0)) <= 1e-12
+    assert abs(lse[0, 0, 0] - math.log(math.exp(x) + 1.0)) <= 1e-12
+    raw = 1.0 / (1.0 + math.exp(-1.1 / math.sqrt(d)))
+    assert abs(o[0, 0, 0, 0] - raw) > 1e-4
+    # head 1: exponent 8, 1e5 / 2^8 = 390.6 rounds to 384: decoded 98304, all weight on key 0
+    assert abs(lse[0, 1, 0] - 98304.0 / math.sqrt(d)) <= 1e-9
+
+
+def test_mxfp8_logits_on_grid_q_is_plain_attention_over_decoded_cache():
+    """q already on the MXFP8 grid (encoded and decoded once) is left as it is,
+    so the result equals attention over the decoded cache exactly."""
+    from oracle import attention_mxfp8_logits, mxfp8_dequantize, mxfp8_quantize
+    rng = np.random.default_rng(31)
+    B, Sq, Skv, Hq, Hkv, d, E = 2, 5, 40, 4, 2, 128, 16
+    x = rng.standard_normal((B, Sq, Hq, d)) * np.exp2(rng.integers(-3, 4, size=(B, Sq, Hq, 1)))
+    q = mxfp8_dequantize(*mxfp8_quantize(x))
+    kc, ks = mxfp8_quantize(rng.standard_normal((B, Skv, Hkv, d)))
+    vc, vs = mxfp8_quantize(rng.standard_normal((B, Skv, Hkv, d)))
+    R = rng.standard_normal((B, Sq, Hq, E)) * 0.3
+    got = attention_mxfp8_logits(q, kc, ks, vc, vs, R, window=17, log_scale_base=64.0)
+    want = attention(q, mxfp8_dequantize(kc, ks), mxfp8_dequantize(vc, vs), R, window=17, log_scale_base=64.0)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+    # and an off-grid q does change the result
+    got2 = attention_mxfp8_logits(x, kc, ks, vc, vs, R, window=17, log_scale_base=64.0)
+    plain = attention(x, mxfp8_dequantize(kc, ks), mxfp8_dequantize(vc, vs), R, window=17, log_scale_base=64.0)
+    assert np.max(np.abs(got2[0] - plain[0])) > 1e-4
