@@ -201,9 +201,10 @@ def cpu_baseline(w, inp, budget_s, *, fixed=(), seed=7, batch=8, sample_note="")
             ("measured_s" if full else "extrapolated_s"): round(t_used if full else total / (work / t_used), 1)}
 
 
-def decode_leg(rba, torch, name, reps, mxfp8=False, leg=None, cpu_budget=0.0):
+def decode_leg(rba, torch, name, reps, mxfp8=False, leg=None, cpu_budget=0.0, qk_fp8=False):
     """One decode workload; mxfp8: its K/V cache encoded to MXFP8 by the library's
-    encoder (timed too) and attention run over the encoded cache.  With
+    encoder (timed too) and attention run over the encoded cache; qk_fp8: the
+    logits in MXFP8 as well (q encoded, QK^T on the scaled FP8 MFMA).  With
     cpu_budget > 0 the oracle is timed on a sample of the same inputs."""
     from workloads import CONFIGS, make_inputs
     w = CONFIGS[name]
@@ -236,7 +237,7 @@ def decode_leg(rba, torch, name, reps, mxfp8=False, leg=None, cpu_budget=0.0):
         del d["k"], d["v"], x, kc, ksc
         torch.cuda.empty_cache()
         a = rba.make_args(d["q"], k8, v8, R, o, None, window=w.window, log_scale_base=w.log_scale_base,
-                          k_scale=ks, v_scale=vs)
+                          k_scale=ks, v_scale=vs, qk_fp8=qk_fp8)
         kv_bytes = kv_bytes * (w.d + w.d // 32) // (2 * w.d)     # codes + scales per bf16 pair of bytes
         keep = (k8, ks, v8, vs)
     else:
@@ -247,7 +248,8 @@ def decode_leg(rba, torch, name, reps, mxfp8=False, leg=None, cpu_budget=0.0):
     ms_warm = time_launches(launch, reps, torch)
     ms = time_cold(launch, max(reps, 50), torch)
     gbs = kv_bytes / (ms * 1e-3) / 1e9
-    kname = "attn_fwd_kernel<bf16, 4 waves" + (", MXFP8>" if mxfp8 else ">") + (" + combine_kernel" if splits > 1 else "")
+    kname = ("attn_fwd_kernel<bf16, 4 waves" + (", MXFP8" if mxfp8 else "") + (" logits" if qk_fp8 else "") + ">"
+             + (" + combine_kernel" if splits > 1 else ""))
     res = {"ms": round(ms, 4), "kv_GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
            "ms_warm": round(ms_warm, 4), "num_splits": splits, "kv_bytes": kv_bytes,
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -256,6 +258,8 @@ def decode_leg(rba, torch, name, reps, mxfp8=False, leg=None, cpu_budget=0.0):
            "timing": "median of 50 launches, each after a 512 MiB read that evicts the caches; ms_warm: back-to-back mean"}
     if mxfp8:
         res["kv_format"] = "MXFP8 (E4M3 codes + E8M0 scale per 32 head-dim entries)"
+        if qk_fp8:
+            res["logits"] = "MXFP8: q encoded per 32 head-dim entries, QK^T on v_mfma_scale_f32_32x32x64_f8f6f4"
     res.update(extra)
     del d, R, o, ws, keep
     torch.cuda.empty_cache()
@@ -571,6 +575,9 @@ def main():
         for name in ("c4_decode_full", "c5_long_decode"):
             extra[name + "_mxfp8"] = decode_leg(rba, torch, name, 20, mxfp8=True)
             extra[name + "_mxfp8"]["cpu_baseline_ref"] = f"workloads.{name} (the oracle runs on the decoded cache)"
+            extra[name + "_mxfp8_logits"] = decode_leg(rba, torch, name, 20, mxfp8=True, qk_fp8=True)
+            extra[name + "_mxfp8_logits"]["cpu_baseline_ref"] = (f"workloads.{name} (the oracle runs on the "
+                                                                 "decoded cache and the encoded q)")
     if extra:
         out["decode_variants"] = extra
     if "prologue" in legs:

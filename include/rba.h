@@ -84,9 +84,16 @@ typedef enum rba_dtype {
 /* Storage of K and V ([S-FA4]). */
 typedef enum rba_kv_format {
     RBA_KV_PLAIN = 0,   /* k, v have the element type dt */
-    RBA_KV_MXFP8 = 1    /* k, v hold OCP E4M3 codes (one byte each); k_scale, v_scale hold one
+    RBA_KV_MXFP8 = 1,   /* k, v hold OCP E4M3 codes (one byte each); k_scale, v_scale hold one
                            E8M0 code per 32 head-dim entries (value 2^(code-127); code 255 is NaN).
                            Attention then runs over the decoded values.  dt must be RBA_BF16. */
+    RBA_KV_MXFP8_QK = 2 /* the cache of RBA_KV_MXFP8, and the logits in MXFP8 as well ([S-FA4]:
+                           the attention kernel runs in an MXFP8 configuration; "vLLM TML Inkling
+                           サポート" names FP8 attention against compute limits): q is encoded with
+                           the cache's rule (blocks of 32 along d) and S = q.K^T is the dot product
+                           of the decoded q and K, on the block-scaled FP8 matrix instruction; the
+                           probabilities and V are as with RBA_KV_MXFP8.  The prologue writes the
+                           same cache for both formats. */
 } rba_kv_format;
 
 /* Shapes, pointers and options of one attention call (prefill or decode).
@@ -94,7 +101,7 @@ typedef enum rba_kv_format {
  *   k, v : [B, Skv, Hkv, d]  strides k_s / v_s = {b, s, h}
  *   R    : [B, Sq, Hq, E]    strides R_s = {b, t, h}; NULL = no bias (E ignored)
  *   lse  : [B, Hq, Sq] fp32, contiguous; NULL = not written
- *   kv_format = RBA_KV_MXFP8: k_scale, v_scale : [B, Skv, Hkv, d/32] bytes,
+ *   kv_format = RBA_KV_MXFP8 or RBA_KV_MXFP8_QK: k_scale, v_scale : [B, Skv, Hkv, d/32] bytes,
  *          strides k_scale_s / v_scale_s = {b, s, h}, the d/32 codes of a row
  *          contiguous (paged: laid out like the pools, {page, key, head}).
  *          k_s / v_s are then byte strides and must be multiples of 16.

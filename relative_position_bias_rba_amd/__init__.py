@@ -31,7 +31,7 @@ lib_path = os.path.join(_HERE, "librba.so")
 RBA_OK, RBA_E_INVALID, RBA_E_UNSUPPORTED, RBA_E_WORKSPACE, RBA_E_LAUNCH = range(5)
 RBA_FP32, RBA_BF16 = 0, 1
 RBA_DECODE_SCRATCH_BYTES = 16 << 20     # size of the scratch array of rba_attn_decode_noalloc
-RBA_KV_PLAIN, RBA_KV_MXFP8 = 0, 1
+RBA_KV_PLAIN, RBA_KV_MXFP8, RBA_KV_MXFP8_QK = 0, 1, 2
 
 
 class RBAError(RuntimeError):
@@ -168,11 +168,12 @@ def _ptr(t):
 
 
 def make_args(q, k, v, R=None, o=None, lse=None, *, window=0, scale=None, log_scale_base=0.0,
-              dt=None, k_scale=None, v_scale=None) -> _AttnArgs:
+              dt=None, k_scale=None, v_scale=None, qk_fp8=False) -> _AttnArgs:
     """Fill the C argument struct from tensors (shapes and strides only).
 
     With k_scale / v_scale given, k and v are MXFP8 codes (uint8) and the
-    scales their E8M0 codes [..., 128/32]."""
+    scales their E8M0 codes [..., 128/32]; qk_fp8=True also encodes q and
+    runs the logits in MXFP8 (rba_kv_format RBA_KV_MXFP8_QK)."""
     a = _AttnArgs()
     B, Sq, Hq, d = q.shape
     a.dt = _dt(q) if dt is None else dt
@@ -192,8 +193,10 @@ def make_args(q, k, v, R=None, o=None, lse=None, *, window=0, scale=None, log_sc
             getattr(a, name)[:] = [t.stride(0), t.stride(1), t.stride(2)]
     if (k_scale is None) != (v_scale is None):
         raise ValueError("give both k_scale and v_scale, or neither")
+    if qk_fp8 and k_scale is None:
+        raise ValueError("qk_fp8 needs an MXFP8 cache (k_scale, v_scale)")
     if k_scale is not None:
-        a.kv_format = RBA_KV_MXFP8
+        a.kv_format = RBA_KV_MXFP8_QK if qk_fp8 else RBA_KV_MXFP8
         a.k_scale, a.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
         for name, t in (("k_scale_s", k_scale), ("v_scale_s", v_scale)):
             if t.dtype != torch.uint8 or t.stride(3) != 1:
@@ -249,15 +252,16 @@ def relproj(r: torch.Tensor, P: torch.Tensor, out_dtype=None, per_head: bool = F
 
 
 def attn_prefill(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0, return_lse=False,
-                 out=None, k_scale=None, v_scale=None):
+                 out=None, k_scale=None, v_scale=None, qk_fp8=False):
     """Attention of every query row over its visible keys (one pass).
-    k_scale / v_scale: K and V are MXFP8 (see mxfp8_quantize)."""
+    k_scale / v_scale: K and V are MXFP8 (see mxfp8_quantize); qk_fp8: the
+    logits in MXFP8 too (q encoded, QK^T on the scaled FP8 matrix unit)."""
     _check_attn_inputs(q, k, v, R, k_scale, v_scale)
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     lse = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=q.device) \
         if return_lse else None
     a = make_args(q, k, v, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base,
-                  k_scale=k_scale, v_scale=v_scale)
+                  k_scale=k_scale, v_scale=v_scale, qk_fp8=qk_fp8)
     _check("rba_attn_prefill", _lib.rba_attn_prefill(ctypes.byref(a), _stream(q.device)))
     return (o, lse) if return_lse else o
 
@@ -343,15 +347,16 @@ def decode_workspace_bytes(q, k, v, R=None, *, window=0, splits=0) -> int:
 
 
 def attn_decode(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0, num_splits=0,
-                return_lse=False, out=None, workspace=None, k_scale=None, v_scale=None):
+                return_lse=False, out=None, workspace=None, k_scale=None, v_scale=None, qk_fp8=False):
     """Split-KV attention of a few query rows against a long KV cache.
-    k_scale / v_scale: K and V are MXFP8 (see mxfp8_quantize)."""
+    k_scale / v_scale: K and V are MXFP8 (see mxfp8_quantize); qk_fp8: the
+    logits in MXFP8 too."""
     _check_attn_inputs(q, k, v, R, k_scale, v_scale)
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     lse = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=q.device) \
         if return_lse else None
     a = make_args(q, k, v, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base,
-                  k_scale=k_scale, v_scale=v_scale)
+                  k_scale=k_scale, v_scale=v_scale, qk_fp8=qk_fp8)
     splits = int(num_splits)
     if splits == 0:
         splits = _lib.rba_num_splits(ctypes.byref(a), 0)
@@ -368,7 +373,7 @@ def attn_decode(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0, nu
 
 
 def attn_decode_noalloc(q, k, v, R=None, *, window=0, scale=None, log_scale_base=0.0, num_splits=0,
-                        out=None, lse=None, k_scale=None, v_scale=None):
+                        out=None, lse=None, k_scale=None, v_scale=None, qk_fp8=False):
     """attn_decode with the split partials in the library's own device
     scratch array (rba_attn_decode_noalloc): the C call allocates nothing.
     Pass `out` (and `lse` [B, Hq, Sq] fp32, optional) to keep this wrapper
@@ -376,7 +381,7 @@ def attn_decode_noalloc(q, k, v, R=None, *, window=0, scale=None, log_scale_base
     _check_attn_inputs(q, k, v, R, k_scale, v_scale)
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     a = make_args(q, k, v, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base,
-                  k_scale=k_scale, v_scale=v_scale)
+                  k_scale=k_scale, v_scale=v_scale, qk_fp8=qk_fp8)
     code = _lib.rba_attn_decode_noalloc(ctypes.byref(a), int(num_splits), _stream(q.device))
     _check("rba_attn_decode_noalloc", code)
     return (o, lse) if lse is not None else o
@@ -399,7 +404,7 @@ def make_paged(block_table, seq_lens, page_size: int, num_pages: int) -> _PagedK
 
 def attn_paged(q, k_pool, v_pool, block_table, seq_lens, R=None, *, max_seq_len=None, window=0, scale=None,
                log_scale_base=0.0, num_splits=0, return_lse=False, out=None, workspace=None, k_scale=None,
-               v_scale=None):
+               v_scale=None, qk_fp8=False):
     """Attention of each sequence's last Sq query rows over its own keys in a
     paged pool k_pool / v_pool [num_pages, page_size, Hkv, 128].
 
@@ -416,7 +421,7 @@ def attn_paged(q, k_pool, v_pool, block_table, seq_lens, R=None, *, max_seq_len=
     if v_pool.shape[:2] != k_pool.shape[:2]:
         raise ValueError("k_pool and v_pool must have the same pages")
     a = make_args(q, k_pool, v_pool, R, o, lse, window=window, scale=scale, log_scale_base=log_scale_base,
-                  k_scale=k_scale, v_scale=v_scale)
+                  k_scale=k_scale, v_scale=v_scale, qk_fp8=qk_fp8)
     a.Skv = int(block_table.shape[1] * page_size if max_seq_len is None else max_seq_len)
     kv = make_paged(block_table, seq_lens, page_size, num_pages)
     splits = int(num_splits)

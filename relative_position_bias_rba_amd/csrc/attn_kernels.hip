@@ -58,6 +58,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int D = 128;                // head size
 constexpr int NT = 256;               // threads per workgroup of the combine kernel
@@ -186,11 +187,16 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16(unsigned w, float sc) {
 // F8: K and V are MXFP8 (E4M3 codes, one E8M0 scale per 32 head-dim entries);
 // both go through registers, are decoded to bf16 exactly and stored in the
 // same LDS layouts as bf16 K and V, so the compute is the bf16 one.
-template <typename T, int NW, bool SLAB2, bool PG, bool F8>
+// FQ (with F8): the logits run in MXFP8 too.  q is encoded once with the
+// cache's rule (blocks of 32 along d), K stays as codes and scales in LDS,
+// and S^T = K . Q^T runs on v_mfma_scale_f32_32x32x64_f8f6f4, which applies
+// the E8M0 scales of both operands itself; V is decoded for PV as with F8.
+template <typename T, int NW, bool SLAB2, bool PG, bool F8, bool FQ = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnParams p) {
     using TL = Tile<T>;
     constexpr bool BF = sizeof(T) == 2;
     static_assert(!F8 || BF, "MXFP8 K/V is decoded to bf16");
+    static_assert(!FQ || F8, "MXFP8 logits need an MXFP8 cache");
     constexpr int ES = (int)sizeof(T);
     constexpr int KES = F8 ? 1 : ES;             // bytes per K/V element in memory
     constexpr int NTH = 64 * NW;                 // threads per workgroup
@@ -282,12 +288,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     const int rb = (prow - N + 1) & ~(CH - 1);
 
     // Q fragment (B operand of S^T = K Q^T), loaded once.
-    constexpr int QREGS = BF ? 8 : 64;
+    constexpr int QREGS = FQ ? 1 : (BF ? 8 : 64);
     typedef typename std::conditional<BF, bf16x8, float>::type QFrag;
     QFrag qf[QREGS];
     {
         const T *qp = (const T *)p.q + (int64_t)b * p.qs0 + (int64_t)tq * p.qs1 + (int64_t)hq * p.qs2;
-        if constexpr (BF) {
+        if constexpr (FQ) {
+            qf[0] = bf16x8{};
+        } else if constexpr (BF) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) qf[k] = cvalid ? *(const bf16x8 *)(qp + 16 * k + 8 * hh) : bf16x8{};
         } else {
@@ -306,6 +314,53 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         // keeps ahead of the LDS reads).
 #pragma unroll
         for (int k = 0; k < QREGS; ++k) asm volatile("" : "+v"(qf[k]));
+    }
+    // FQ: q encoded to MXFP8 as the B operand of the scaled MFMA.  For k-step
+    // ks (64 head-dim entries), lane (column, half hh) holds the codes of
+    // entries 64ks + 16hh + [0, 16) in bytes 0-15 and 64ks + 32 + 16hh +
+    // [0, 16) in bytes 16-31; the instruction takes the scale of the block of
+    // bytes 0-15 (entries 64ks .. 64ks+31) from the lower-half lane and that
+    // of bytes 16-31 from the upper-half lane (lane layout checked on the
+    // device).  So each block of 32 is split over the two halves of a
+    // column, which exchange their maxima; encoding as the cache encoder
+    // does: exponent floor(log2 max) - 8 clamped to [-127, 127] (-127 for a
+    // zero block), exact scaling, saturation to 448, hardware RNE conversion.
+    i32x8 q8[FQ ? 2 : 1] = {};
+    int qsc[FQ ? 2 : 1] = {};
+    if constexpr (FQ) {
+        const T *qp = (const T *)p.q + (int64_t)b * p.qs0 + (int64_t)tq * p.qs1 + (int64_t)hq * p.qs2;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const int d0 = 32 * blk + 16 * hh;
+            const bf16x8 x0 = cvalid ? *(const bf16x8 *)(qp + d0) : bf16x8{};
+            const bf16x8 x1 = cvalid ? *(const bf16x8 *)(qp + d0 + 8) : bf16x8{};
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                v[i] = (float)x0[i];
+                v[8 + i] = (float)x1[i];
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            int e = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 1 - 8 : -127;
+            e = min(max(e, -127), 127);
+            int w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float s0 = fminf(fmaxf(ldexpf(v[4 * i], -e), -448.f), 448.f);
+                const float s1 = fminf(fmaxf(ldexpf(v[4 * i + 1], -e), -448.f), 448.f);
+                const float s2 = fminf(fmaxf(ldexpf(v[4 * i + 2], -e), -448.f), 448.f);
+                const float s3 = fminf(fmaxf(ldexpf(v[4 * i + 3], -e), -448.f), 448.f);
+                w[i] = __builtin_amdgcn_cvt_pk_fp8_f32(s2, s3, __builtin_amdgcn_cvt_pk_fp8_f32(s0, s1, 0, false), true);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) q8[blk >> 1][4 * (blk & 1) + i] = w[i];
+            qsc[blk >> 1] = (blk & 1) == hh ? e + 127 : qsc[blk >> 1];
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) asm volatile("" : "+v"(q8[ks]), "+v"(qsc[ks]));
     }
 
     f32x16 O[4];
@@ -427,19 +482,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     // vector-memory instructions one load8 issues
     constexpr int kLoad8Ops = 4 * NP8;
 
+    // FQ: K stays MXFP8 in LDS: row r of codes at byte K8R * r, the four
+    // scale bytes of row r at K8S + 4 r.
+    constexpr int K8R = D + 16;                 // padded code row (bytes)
+    constexpr int K8S = N * K8R;
+    static_assert(!FQ || K8S + 4 * N <= (int)sizeof(sK), "K codes and scales fit the K buffer");
+    unsigned char *const sK8 = (unsigned char *)&sK[0][0];
+
     // F8: decode register set X into the K and V buffers (bf16)
     auto store8 = [&](const F8Set &X) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NP8; ++i) {
             const float sk = e8m0_scale(X.ks[i]), sv = e8m0_scale(X.vs[i]);
-            u32x2 a = e4m3x4_to_bf16(X.k[i][0], sk), b2 = e4m3x4_to_bf16(X.k[i][1], sk);
-            u32x2 c = e4m3x4_to_bf16(X.k[i][2], sk), d = e4m3x4_to_bf16(X.k[i][3], sk);
-            T *dst = &sK[0][k8d + i * RSTEP * KS];
-            *(u32x4 *)dst = u32x4{a[0], a[1], b2[0], b2[1]};
-            *(u32x4 *)(dst + 8) = u32x4{c[0], c[1], d[0], d[1]};
-            a = e4m3x4_to_bf16(X.v[i][0], sv), b2 = e4m3x4_to_bf16(X.v[i][1], sv);
-            c = e4m3x4_to_bf16(X.v[i][2], sv), d = e4m3x4_to_bf16(X.v[i][3], sv);
-            dst = &sV[v8d + i * RSTEP * D];
+            if constexpr (FQ) {
+                const int row = (tid >> 3) + i * RSTEP, c = tid & 7;
+                *(u32x4 *)&sK8[row * K8R + 16 * c] = X.k[i];
+                if ((c & 1) == 0) sK8[K8S + 4 * row + (c >> 1)] = (unsigned char)X.ks[i];
+            } else {
+                u32x2 a = e4m3x4_to_bf16(X.k[i][0], sk), b2 = e4m3x4_to_bf16(X.k[i][1], sk);
+                u32x2 c = e4m3x4_to_bf16(X.k[i][2], sk), d = e4m3x4_to_bf16(X.k[i][3], sk);
+                T *dst = &sK[0][k8d + i * RSTEP * KS];
+                *(u32x4 *)dst = u32x4{a[0], a[1], b2[0], b2[1]};
+                *(u32x4 *)(dst + 8) = u32x4{c[0], c[1], d[0], d[1]};
+            }
+            u32x2 a = e4m3x4_to_bf16(X.v[i][0], sv), b2 = e4m3x4_to_bf16(X.v[i][1], sv);
+            u32x2 c = e4m3x4_to_bf16(X.v[i][2], sv), d = e4m3x4_to_bf16(X.v[i][3], sv);
+            T *dst = &sV[v8d + i * RSTEP * D];
             *(u32x4 *)dst = u32x4{a[0], a[1], b2[0], b2[1]};
             *(u32x4 *)(dst + 8) = u32x4{c[0], c[1], d[0], d[1]};
         }
@@ -558,7 +626,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 
         // S^T = K . Q^T
         const T *kb_ = k_lane + buf * (N * KS);
-        if constexpr (BF) {
+        if constexpr (FQ) {
+            // A operand: key row 32u + mfma_row_key(lc), entries 64ks + 16hh
+            // + [0, 16) and 64ks + 32 + 16hh + [0, 16); its scale is the
+            // row's block 2ks + hh (see the q encoding above)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int u = 0; u < KT; ++u) {
+                    const int kr = 32 * u + mfma_row_key(lc);
+                    const unsigned char *src = sK8 + kr * K8R + 64 * ks + 16 * hh;
+                    const u32x4 lo = *(const u32x4 *)src, hi = *(const u32x4 *)(src + 32);
+                    const i32x8 a = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    const int sa = sK8[K8S + 4 * kr + 2 * ks + hh];
+                    S[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q8[ks], S[u], 0, 0, 0, sa, 0, qsc[ks]);
+                }
+            }
+        } else if constexpr (BF) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
 #pragma unroll
@@ -1615,9 +1700,16 @@ hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stre
     // K/V in plain bf16 or fp32 (the pp kernel needs 32-bit K/V offsets), or MXFP8
 #define RBA_FWD(T, NW, SLAB2, PG, F8)                                                                   \
     hipLaunchKernelGGL((attn_fwd_kernel<T, NW, SLAB2, PG, F8>), grid, dim3(64 * NW), 0, stream, p)
+#define RBA_FWDQ(NW, SLAB2, PG)                                                                         \
+    hipLaunchKernelGGL((attn_fwd_kernel<__bf16, NW, SLAB2, PG, true, true>), grid, dim3(64 * NW), 0, stream, p)
+    const bool fq = f8 && p.qk8;
     switch (v) {
         case AttnVariant::BF16_WIDE:    // 8 waves, 256 columns
-            if (f8 && paged)
+            if (fq && paged)
+                RBA_FWDQ(8, true, true);
+            else if (fq)
+                RBA_FWDQ(8, true, false);
+            else if (f8 && paged)
                 RBA_FWD(__bf16, 8, true, true, true);
             else if (f8)
                 RBA_FWD(__bf16, 8, true, false, true);
@@ -1629,7 +1721,11 @@ hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stre
                 RBA_FWD(__bf16, 8, true, false, false);
             break;
         case AttnVariant::BF16_NARROW:  // 4 waves: 128 columns, small LDS footprint
-            if (f8 && paged)
+            if (fq && paged)
+                RBA_FWDQ(4, false, true);
+            else if (fq)
+                RBA_FWDQ(4, false, false);
+            else if (f8 && paged)
                 RBA_FWD(__bf16, 4, false, true, true);
             else if (f8)
                 RBA_FWD(__bf16, 4, false, false, true);
@@ -1647,6 +1743,7 @@ hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stre
             break;
     }
 #undef RBA_FWD
+#undef RBA_FWDQ
     return hipGetLastError();
 }
 

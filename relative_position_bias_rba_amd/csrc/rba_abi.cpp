@@ -30,13 +30,14 @@ bool strides_ok(const int64_t s[3], int64_t mult) {
 }
 
 // Bytes per K/V element in memory.
-int kv_elem_size(const rba_attn_args *a) { return a->kv_format == RBA_KV_MXFP8 ? 1 : elem_size(a->dt); }
+bool kv_mx(const rba_attn_args *a) { return a->kv_format == RBA_KV_MXFP8 || a->kv_format == RBA_KV_MXFP8_QK; }
+int kv_elem_size(const rba_attn_args *a) { return kv_mx(a) ? 1 : elem_size(a->dt); }
 
 rba_status validate_attn(const rba_attn_args *a) {
     if (a == nullptr) return RBA_E_INVALID;
     if (a->dt != RBA_BF16 && a->dt != RBA_FP32) return RBA_E_UNSUPPORTED;
-    if (a->kv_format != RBA_KV_PLAIN && a->kv_format != RBA_KV_MXFP8) return RBA_E_INVALID;
-    if (a->kv_format == RBA_KV_MXFP8 && a->dt != RBA_BF16) return RBA_E_UNSUPPORTED;
+    if (a->kv_format != RBA_KV_PLAIN && !kv_mx(a)) return RBA_E_INVALID;
+    if (kv_mx(a) && a->dt != RBA_BF16) return RBA_E_UNSUPPORTED;
     if (a->d <= 0) return RBA_E_INVALID;
     if (a->d != kHeadDim) return RBA_E_UNSUPPORTED;
     if (a->B < 0 || a->Sq < 0 || a->Skv < 0 || a->Hq < 1 || a->Hkv < 1) return RBA_E_INVALID;
@@ -57,7 +58,7 @@ rba_status validate_attn(const rba_attn_args *a) {
     const int64_t kch = 16 / kv_elem_size(a);
     if (!strides_ok(a->q_s, ch) || !strides_ok(a->k_s, kch) || !strides_ok(a->v_s, kch) || !strides_ok(a->o_s, ch))
         return RBA_E_INVALID;
-    if (a->kv_format == RBA_KV_MXFP8) {
+    if (kv_mx(a)) {
         if (a->k_scale == nullptr || a->v_scale == nullptr) return RBA_E_INVALID;
         if (!strides_ok(a->k_scale_s, 1) || !strides_ok(a->v_scale_s, 1)) return RBA_E_INVALID;
     }
@@ -146,8 +147,9 @@ rba::AttnParams make_params(const rba_attn_args *a, const Plan &pl, int splits) 
               a->R_s[1] % ch == 0 && a->R_s[2] % ch == 0;
     const int64_t kv_row = std::max(a->k_s[1], a->v_s[1]);
     p.kv32 = ((int64_t)a->Skv * kv_row + kHeadDim) * elem_size(a->dt) < ((int64_t)1 << 31);
-    if (a->kv_format == RBA_KV_MXFP8) {
+    if (kv_mx(a)) {
         p.kv32 = 0;   // the MXFP8 path is the register-staged kernel
+        p.qk8 = a->kv_format == RBA_KV_MXFP8_QK;
         p.k_scale = (const uint8_t *)a->k_scale;
         p.v_scale = (const uint8_t *)a->v_scale;
         p.kss0 = a->k_scale_s[0], p.kss1 = a->k_scale_s[1], p.kss2 = a->k_scale_s[2];
@@ -364,7 +366,7 @@ rba_status rba_attn_prologue(const rba_prologue_args *a, const rba_attn_args *c,
                              void *stream) {
     if (a == nullptr || c == nullptr) return RBA_E_INVALID;
     if (c->dt != RBA_BF16) return RBA_E_UNSUPPORTED;
-    if (c->kv_format != RBA_KV_PLAIN && c->kv_format != RBA_KV_MXFP8) return RBA_E_INVALID;
+    if (c->kv_format != RBA_KV_PLAIN && !kv_mx(c)) return RBA_E_INVALID;
     if (a->d != kHeadDim || c->d != kHeadDim) return a->d <= 0 ? RBA_E_INVALID : RBA_E_UNSUPPORTED;
     if (a->B < 0 || a->T < 0 || a->Hq < 1 || a->Hkv < 1 || a->Hkv != c->Hkv || c->Skv < 1) return RBA_E_INVALID;
     if (a->conv_w < 1 || a->conv_w > kMaxConvTaps) return RBA_E_INVALID;
@@ -390,7 +392,7 @@ rba_status rba_attn_prologue(const rba_prologue_args *a, const rba_attn_args *c,
     if (!aligned(a->cu_new, 4) || !aligned(a->seq_lens, 4) || !aligned(a->conv_wk, 4) || !aligned(a->conv_wv, 4) ||
         !aligned(a->norm_q, 4) || !aligned(a->norm_k, 4))
         return RBA_E_INVALID;
-    const bool f8 = c->kv_format == RBA_KV_MXFP8;
+    const bool f8 = kv_mx(c);
     if (f8 && (c->k_scale == nullptr || c->v_scale == nullptr || !strides_ok(c->k_scale_s, 1) ||
                !strides_ok(c->v_scale_s, 1)))
         return RBA_E_INVALID;

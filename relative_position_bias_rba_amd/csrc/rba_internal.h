@@ -42,6 +42,7 @@ struct AttnParams {
     // (bytes) laid out like k and v (paged: page, key, head).
     const uint8_t *k_scale, *v_scale;
     int64_t kss0, kss1, kss2, vss0, vss1, vss2;
+    int qk8;             // MXFP8 logits: q encoded too, S = QK^T on the scaled FP8 MFMA
     // Relative logits computed inside the prefill kernel (rf != null; then
     // R is null): relative features rf [B, Sq, (Hq,) r_dim] with strides
     // rfs0..2 (rfs2 = 0: shared by the heads), the projection packed by

@@ -204,8 +204,19 @@ def test_mxfp8_kv_validation():
     ks = torch.zeros(*k.shape[:3], 4, dtype=torch.uint8)
     a = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks)
     assert a.kv_format == rba.RBA_KV_MXFP8
-    a2 = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks); a2.kv_format = 2
+    a2 = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks); a2.kv_format = 3
     assert _prefill(a2) == RBA_E_INVALID
+    # the MXFP8-logits format takes the same cache and the same checks
+    a3 = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks, qk_fp8=True)
+    assert a3.kv_format == rba.RBA_KV_MXFP8_QK == 2
+    a3.dt = 0
+    assert _prefill(a3) == RBA_E_UNSUPPORTED and _decode(a3) == RBA_E_UNSUPPORTED
+    a3 = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks, qk_fp8=True); a3.v_scale = None
+    assert _prefill(a3) == RBA_E_INVALID and _decode(a3) == RBA_E_INVALID
+    a3 = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks, qk_fp8=True); a3.k_s[1] = 136
+    assert _decode(a3) == RBA_E_INVALID
+    with pytest.raises(ValueError):
+        make_args(q, k, v, R, o, qk_fp8=True)
     a2 = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks); a2.dt = 0
     assert _prefill(a2) == RBA_E_UNSUPPORTED and _decode(a2) == RBA_E_UNSUPPORTED
     a2 = make_args(q, kc, kc, R, o, k_scale=ks, v_scale=ks); a2.k_scale = None

@@ -225,3 +225,95 @@ def test_attention_mxfp8_full_size_sampled():
     got_l = torch.stack([lse[b, :, t] for b, t in rows])
     check("full-size mxfp8 o", got_o, wo)
     check("full-size mxfp8 lse", got_l, wl, fp32=True, tol=2e-2)
+
+
+# --------------------------------------------------------------------------- MXFP8 logits (q encoded, scaled FP8 MFMA)
+
+@pytest.mark.parametrize("name,over,splits", F8_CASES, ids=[c[0] for c in F8_CASES])
+def test_attention_mxfp8_logits_parity(name, over, splits):
+    """rba_kv_format RBA_KV_MXFP8_QK against oracle.attention_mxfp8_logits on
+    every element (q encoded with the cache's rule, logits of the decoded q
+    and K, V decoded)."""
+    m = rba()
+    w = scaled(CONFIGS["c4_decode_full"], **over)
+    say(f"mxfp8 logits {name}: {w}")
+    inp = _f8_inputs(w)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    R = m.relproj(d["r"], d["P"])
+    Rw = oracle.relproj(inp["r"], inp["P"])
+    wo, wl = oracle.attention_mxfp8_logits(inp["q"], inp["kc"].numpy(), inp["ks"].numpy(), inp["vc"].numpy(),
+                                           inp["vs"].numpy(), Rw, window=w.window, log_scale_base=w.log_scale_base)
+    kw = dict(window=w.window, log_scale_base=w.log_scale_base, return_lse=True, k_scale=d["ks"], v_scale=d["vs"],
+              qk_fp8=True)
+    outs = []
+    for s in splits:
+        o, lse = m.attn_decode(d["q"], d["kc"], d["vc"], R, num_splits=s, **kw)
+        torch.cuda.synchronize()
+        check(f"{name}/{s} o", o, wo)
+        check(f"{name}/{s} lse", lse, wl, fp32=True, tol=2e-2)
+        outs.append(lse)
+    # the encoded q moves the logits: the result is measurably not the plain
+    # MXFP8-cache attention (bf16 q), which the oracle computes separately
+    wp, _ = oracle.attention(inp["q"], inp["kd"], inp["vd"], Rw, window=w.window, log_scale_base=w.log_scale_base)
+    g = o.double().cpu().numpy()
+    assert np.linalg.norm(g - wo) < 0.5 * np.linalg.norm(g - wp), name
+    if name == "wide_prefill":
+        o, lse = m.attn_prefill(d["q"], d["kc"], d["vc"], R, **kw)
+        torch.cuda.synchronize()
+        check(f"{name} prefill o", o, wo)
+        check(f"{name} prefill lse", lse, wl, fp32=True, tol=2e-2)
+
+
+def test_attention_mxfp8_logits_paged():
+    m = rba()
+    w = scaled(CONFIGS["c4_decode_full"], B=4, Sq=9, Skv=640, Hq=16, Hkv=2, E=64, window=0)
+    inp = make_paged_inputs(w, 64, seq_lens=[9, 640, 200, 65])
+    kc, ks = quantize_cpu(inp["k_pool"])
+    vc, vs = quantize_cpu(inp["v_pool"])
+    Rw = oracle.relproj(inp["r"], inp["P"])
+    kd = oracle.mxfp8_dequantize(kc.numpy(), ks.numpy())
+    vd = oracle.mxfp8_dequantize(vc.numpy(), vs.numpy())
+    qd = oracle.mxfp8_dequantize(*oracle.mxfp8_quantize(inp["q"]))
+    wo, wl = oracle.attention_paged(qd, kd, vd, inp["block_table"], inp["seq_lens"], Rw)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    R = m.relproj(d["r"], d["P"])
+    for s in (1, 4):
+        o, lse = m.attn_paged(d["q"], kc.to(DEV), vc.to(DEV), d["block_table"], d["seq_lens"], R, max_seq_len=w.Skv,
+                              num_splits=s, return_lse=True, k_scale=ks.to(DEV), v_scale=vs.to(DEV), qk_fp8=True)
+        torch.cuda.synchronize()
+        check(f"paged mxfp8 logits/{s} o", o, wo)
+        check(f"paged mxfp8 logits/{s} lse", lse, wl, fp32=True, tol=2e-2)
+
+
+@pytest.mark.parametrize("name,rows", [
+    ("c4_decode_full", [(0, 0), (0, 8), (17, 4), (63, 8)]),
+    ("c5_long_decode", [(0, 0)]),
+])
+def test_attention_mxfp8_logits_full_size_sampled(name, rows):
+    """The full decode workloads over an MXFP8 cache (oracle-encoded template
+    rows, as in the test above) with MXFP8 logits, heuristic splits; sampled
+    rows against the oracle."""
+    m = rba()
+    w = CONFIGS[name]
+    tmpl = make_inputs(scaled(w, Skv=4096, B=1, Sq=1))
+    tk, tks = quantize_cpu(tmpl["k"][0])
+    tv, tvs = quantize_cpu(tmpl["v"][0])
+    g = torch.Generator().manual_seed(505)
+    idx = torch.randint(0, 4096, (w.B, w.Skv), generator=g)
+    kc, ks, vc, vs = tk[idx], tks[idx], tv[idx], tvs[idx]
+    inp = make_inputs(scaled(w, Skv=w.Sq))   # q, r, P at full size (k, v unused)
+    d = {k: v.to(DEV) for k, v in inp.items() if k in ("q", "r", "P")}
+    R = m.relproj(d["r"], d["P"])
+    o, lse = m.attn_decode(d["q"], kc.to(DEV), vc.to(DEV), R, k_scale=ks.to(DEV), v_scale=vs.to(DEV),
+                           window=w.window, log_scale_base=w.log_scale_base, return_lse=True, qk_fp8=True)
+    torch.cuda.synchronize()
+    # the oracle over the sampled sequences only (batch index i of bs[i])
+    bs = sorted({b for b, _ in rows})
+    kd = torch.stack([torch.from_numpy(oracle.mxfp8_dequantize(kc[b].numpy(), ks[b].numpy())) for b in bs])
+    vd = torch.stack([torch.from_numpy(oracle.mxfp8_dequantize(vc[b].numpy(), vs[b].numpy())) for b in bs])
+    qd = torch.from_numpy(oracle.mxfp8_dequantize(*oracle.mxfp8_quantize(inp["q"][bs])))
+    Rw = lambda i, t: oracle.relproj(inp["r"][bs[i], t], inp["P"])
+    sel = [(bs.index(b), t) for b, t in rows]
+    wo, wl = oracle.attention_rows(qd, kd, vd, Rw, sel, window=w.window, log_scale_base=w.log_scale_base)
+    check(f"{name} mxfp8 logits o", torch.stack([o[b, t] for b, t in rows]), wo)
+    check(f"{name} mxfp8 logits lse", torch.stack([lse[b, :, t] for b, t in rows]), wl, fp32=True, tol=2e-2)
