@@ -66,6 +66,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;  // log2 growth of the running max tolerated before O is rescaled
 constexpr float kRescaleLimit = 256.f;   // 2^kRescaleSlack
+constexpr int kPrioPeriod = 16;          // decode: key tiles per wave-priority phase
 
 template <typename T>
 struct Tile;
@@ -813,6 +814,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         return kt;
     };
 
+    // Two workgroups share a CU and the older one's waves win issue ties, so
+    // with equal work the younger one finishes last and the launch waits for
+    // it.  The wave priority therefore alternates every kPrioPeriod tiles, in
+    // opposite phase for the two halves of the grid (the halves that were
+    // dispatched as first and second workgroup of a CU), so both progress
+    // alike on average.
+    auto fair_prio = [&](int it) __attribute__((always_inline)) {
+        if constexpr (NW == 4) {
+            if ((((it / kPrioPeriod) + (blockIdx.x >= gridDim.x / 2)) & 1) != 0)
+                __builtin_amdgcn_s_setprio(1);
+            else
+                __builtin_amdgcn_s_setprio(0);
+        }
+    };
     int kt = n_it > 0 ? next_tile() : 0;
     if constexpr (F8) {
         // Two tiles in flight: while tile kt is computed from LDS, the codes of
@@ -832,6 +847,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         }
         __syncthreads();
         auto body = [&](int it, F8Set &X, F8Set &Y) __attribute__((always_inline)) {
+            fair_prio(it);
             const bool nxt = it + 1 < n_it, nxt2 = it + 2 < n_it;
             const int kn2 = nxt2 ? next_tile() : kn;
             const int sb = it & 1;                       // bias buffer of kt; kn's is sb ^ 1
@@ -871,6 +887,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     }
     if (!F8) __syncthreads();
     for (int it = 0; it < (F8 ? 0 : n_it); ++it) {
+        fair_prio(it);
         const int cur = it & 1;
         const bool nxt = it + 1 < n_it;
         const int kn = nxt ? next_tile() : kt;
