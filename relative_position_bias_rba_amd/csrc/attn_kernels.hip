@@ -1436,8 +1436,11 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
             }
         }
         burst(6, 11);
-        // Probabilities against the current reference max m (exp2 domain);
-        // row sums over the same bf16 values the PV product uses.
+        // Probabilities against the current reference max m (exp2 domain),
+        // rounded to bf16 for the PV product; the row sum adds the fp32 values
+        // in two chains.  (A v_dot2c sum over the bf16 values keeps numerator
+        // and denominator on the same rounding, but those instructions stall
+        // next to the other wave's MFMAs; full-causal workload 31.0 -> 30.2 ms.)
         const float sa = amul;
         float sum = 0.f;
         auto exps = [&](float mu, auto dma_b) __attribute__((always_inline)) {
@@ -1449,11 +1452,11 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
                 for (int h2 = 0; h2 < 2; ++h2) {
                     bf16x8 pb;
 #pragma unroll
-                    for (int x = 0; x < 8; ++x) pb[x] = (__bf16)fast_exp2(fmaf(S[u][8 * h2 + x], sa, -mu));
-#pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        sm[x & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[2 * x], pb[2 * x + 1]},
-                                                              bf16x2{(__bf16)1.f, (__bf16)1.f}, sm[x & 1], false);
+                    for (int x = 0; x < 8; ++x) {
+                        const float e = fast_exp2(fmaf(S[u][8 * h2 + x], sa, -mu));
+                        pb[x] = (__bf16)e;
+                        sm[x & 1] += e;
+                    }
                     P[2 * u + h2] = pb;
                     if constexpr (DB) {
                         if (u == 0 && h2 == 0) burst(11, 15);
