@@ -46,11 +46,11 @@ def log(*a):
 # (factors from a plain 1 GiB device copy under the same counters), keyed by leg and by the sha256
 # prefix of the kernel source the counters were taken on; any other source reports null.
 PROFILED_TRAFFIC = {
-    ("c3", "6817485253b01795"): 6563373 * 1024 * 2 + 1049089 * 1024,
-    ("c2", "6817485253b01795"): 511470 * 1024 * 2 + 131606 * 1024,
-    ("c4w", "6817485253b01795"): 578572 * 1024 * 2 + 9216 * 1024,
-    ("c4f", "6817485253b01795"): 1225740 * 1024 * 2 + 9216 * 1024,
-    ("c5", "6817485253b01795"): 524498 * 1024 * 2 + 2064 * 1024,
+    ("c3", "dae4d5990f40104b"): 6534720 * 1024 * 2 + 1049088 * 1024,
+    ("c2", "dae4d5990f40104b"): 509203 * 1024 * 2 + 131596 * 1024,
+    ("c4w", "dae4d5990f40104b"): 578573 * 1024 * 2 + 9216 * 1024,
+    ("c4f", "dae4d5990f40104b"): 1225742 * 1024 * 2 + 9216 * 1024,
+    ("c5", "dae4d5990f40104b"): 524494 * 1024 * 2 + 2064 * 1024,
 }
 
 
