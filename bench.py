@@ -48,9 +48,6 @@ def log(*a):
 PROFILED_TRAFFIC = {
     ("c3", "dae4d5990f40104b"): 6534720 * 1024 * 2 + 1049088 * 1024,
     ("c2", "dae4d5990f40104b"): 509203 * 1024 * 2 + 131596 * 1024,
-    ("c4w", "dae4d5990f40104b"): 578573 * 1024 * 2 + 9216 * 1024,
-    ("c4f", "dae4d5990f40104b"): 1225742 * 1024 * 2 + 9216 * 1024,
-    ("c5", "dae4d5990f40104b"): 524494 * 1024 * 2 + 2064 * 1024,
 }
 
 
@@ -208,7 +205,12 @@ def decode_leg(rba, torch, name, reps, mxfp8=False, leg=None, cpu_budget=0.0, qk
     """One decode workload; mxfp8: its K/V cache encoded to MXFP8 by the library's
     encoder (timed too) and attention run over the encoded cache; qk_fp8: the
     logits in MXFP8 as well (q encoded, QK^T on the scaled FP8 MFMA).  With
-    cpu_budget > 0 the oracle is timed on a sample of the same inputs."""
+    cpu_budget > 0 the oracle is timed on a sample of the same inputs.
+
+    The cache is stored head-major, [B, Hkv, Skv, d] (codes and scales alike),
+    and handed over as a [B, Skv, Hkv, d] view with those strides: each key
+    tile of one kv head is then one contiguous block.  The bf16 legs also time
+    the token-major cache ([B, Skv, Hkv, d] contiguous) with the same values."""
     from workloads import CONFIGS, make_inputs
     w = CONFIGS[name]
     log(f"decode {name}{' mxfp8' if mxfp8 else ''}: generating inputs")
@@ -224,6 +226,18 @@ def decode_leg(rba, torch, name, reps, mxfp8=False, leg=None, cpu_budget=0.0, qk
     st = rba._stream(d["q"].device)
     extra = {}
     kv_bytes = w.kv_bytes()
+    kh = d["k"].transpose(1, 2).contiguous()          # head-major storage [B, Hkv, Skv, d]
+    vh = d["v"].transpose(1, 2).contiguous()
+    if not mxfp8:
+        a_tm = rba.make_args(d["q"], d["k"], d["v"], R, o, None, window=w.window, log_scale_base=w.log_scale_base)
+        launch_tm = c_launcher(rba, "rba_attn_decode", ctypes.byref(a_tm), splits, ctypes.c_void_p(ws.data_ptr()),
+                               ws.numel(), st)
+        time_launches(launch_tm, 5, torch)
+        ms_tm = time_cold(launch_tm, max(reps, 50), torch)
+        gbs_tm = kv_bytes / (ms_tm * 1e-3) / 1e9
+        extra["token_major"] = {"ms": round(ms_tm, 4), "kv_GBps": round(gbs_tm, 1),
+                                "frac_hbm": round(gbs_tm / PEAK_HBM_GBS, 4),
+                                "cache": "[B, Skv, Hkv, d] contiguous, same values"}
     if mxfp8:
         x = d["k"].reshape(-1, w.d)
         kc = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
@@ -235,17 +249,21 @@ def decode_leg(rba, torch, name, reps, mxfp8=False, leg=None, cpu_budget=0.0, qk
         extra["encode_k"] = {"ms": round(ms_enc, 4), "GBps": round(enc_bytes / (ms_enc * 1e-3) / 1e9, 1),
                              "frac_hbm": round(enc_bytes / (ms_enc * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                              "bytes": enc_bytes}
-        k8, ks = rba.mxfp8_quantize(d["k"])
-        v8, vs = rba.mxfp8_quantize(d["v"])
-        del d["k"], d["v"], x, kc, ksc
+        k8, ks = rba.mxfp8_quantize(kh)
+        v8, vs = rba.mxfp8_quantize(vh)
+        k8, ks, v8, vs = (t.transpose(1, 2) for t in (k8, ks, v8, vs))
+        del d["k"], d["v"], x, kc, ksc, kh, vh
         torch.cuda.empty_cache()
         a = rba.make_args(d["q"], k8, v8, R, o, None, window=w.window, log_scale_base=w.log_scale_base,
                           k_scale=ks, v_scale=vs, qk_fp8=qk_fp8)
         kv_bytes = kv_bytes * (w.d + w.d // 32) // (2 * w.d)     # codes + scales per bf16 pair of bytes
         keep = (k8, ks, v8, vs)
     else:
-        a = rba.make_args(d["q"], d["k"], d["v"], R, o, None, window=w.window, log_scale_base=w.log_scale_base)
-        keep = ()
+        del d["k"], d["v"]
+        torch.cuda.empty_cache()
+        a = rba.make_args(d["q"], kh.transpose(1, 2), vh.transpose(1, 2), R, o, None, window=w.window,
+                          log_scale_base=w.log_scale_base)
+        keep = (kh, vh)
     launch = c_launcher(rba, "rba_attn_decode", ctypes.byref(a), splits, ctypes.c_void_p(ws.data_ptr()),
                         ws.numel(), st)
     ms_warm = time_launches(launch, reps, torch)
@@ -255,8 +273,9 @@ def decode_leg(rba, torch, name, reps, mxfp8=False, leg=None, cpu_budget=0.0, qk
              + (" + combine_kernel" if splits > 1 else ""))
     res = {"ms": round(ms, 4), "kv_GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
            "ms_warm": round(ms_warm, 4), "num_splits": splits, "kv_bytes": kv_bytes,
+           "cache": "head-major [B, Hkv, Skv, d] storage, passed as a strided [B, Skv, Hkv, d] view",
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic(leg) if leg else None,
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic(leg + "/head-major") if leg else None,
                         "kernel": kname, "avg_ms": round(ms, 4), "algorithmic_bytes": kv_bytes},
            "timing": "median of 50 launches, each after a 512 MiB read that evicts the caches; ms_warm: back-to-back mean"}
     if mxfp8:
@@ -275,7 +294,8 @@ def decode_leg(rba, torch, name, reps, mxfp8=False, leg=None, cpu_budget=0.0, qk
 
 def paged_decode_leg(rba, torch, name, page_size, reps, len_lo, seed=77):
     """The decode workload with its cache in page_size-key pages of a shared pool
-    and each sequence's length drawn uniformly from [len_lo, Skv]."""
+    and each sequence's length drawn uniformly from [len_lo, Skv].  Each page is
+    stored head-major ([Hkv, page_size, d]); the token-major pool is timed too."""
     from workloads import CONFIGS, make_paged_inputs
     w = CONFIGS[name]
     g = torch.Generator().manual_seed(seed)
@@ -286,15 +306,24 @@ def paged_decode_leg(rba, torch, name, page_size, reps, len_lo, seed=77):
     del inp
     R = rba.relproj(d["r"], d["P"])
     o = torch.empty_like(d["q"])
-    a = rba.make_args(d["q"], d["k_pool"], d["v_pool"], R, o, None, window=w.window,
-                      log_scale_base=w.log_scale_base)
-    a.Skv = w.Skv
     kv = rba.make_paged(d["block_table"], d["seq_lens"], page_size, d["k_pool"].shape[0])
-    splits = rba._lib.rba_num_splits(ctypes.byref(a), 0)
-    need = rba._lib.rba_decode_workspace_bytes(ctypes.byref(a), splits)
-    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-    launch = c_launcher(rba, "rba_attn_paged", ctypes.byref(a), ctypes.byref(kv), splits,
-                        ctypes.c_void_p(ws.data_ptr()), ws.numel(), rba._stream(d["q"].device))
+
+    def launcher(kp, vp):
+        a = rba.make_args(d["q"], kp, vp, R, o, None, window=w.window, log_scale_base=w.log_scale_base)
+        a.Skv = w.Skv
+        splits = rba._lib.rba_num_splits(ctypes.byref(a), 0)
+        need = rba._lib.rba_decode_workspace_bytes(ctypes.byref(a), splits)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        return splits, (a, ws), c_launcher(rba, "rba_attn_paged", ctypes.byref(a), ctypes.byref(kv), splits,
+                                           ctypes.c_void_p(ws.data_ptr()), ws.numel(), rba._stream(d["q"].device))
+
+    splits, keep_tm, launch_tm = launcher(d["k_pool"], d["v_pool"])
+    time_launches(launch_tm, 5, torch)
+    ms_tm = time_cold(launch_tm, max(reps, 50), torch)
+    kh = d["k_pool"].transpose(1, 2).contiguous().transpose(1, 2)
+    vh = d["v_pool"].transpose(1, 2).contiguous().transpose(1, 2)
+    del d["k_pool"], d["v_pool"], keep_tm
+    splits, keep, launch = launcher(kh, vh)
     ms_warm = time_launches(launch, reps, torch)
     ms = time_cold(launch, max(reps, 50), torch)
     # K and V of the keys the rows see (window 0: every key of the sequence)
@@ -306,8 +335,11 @@ def paged_decode_leg(rba, torch, name, page_size, reps, len_lo, seed=77):
     res = {"ms": round(ms, 4), "kv_GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
            "ms_warm": round(ms_warm, 4), "num_splits": splits, "kv_bytes": kv_bytes, "page_size": page_size,
            "seq_lens": f"uniform in [{len_lo}, {w.Skv}], seed {seed}",
+           "cache": "pages stored head-major [Hkv, page_size, d], passed as strided [page_size, Hkv, d] views",
+           "token_major": {"ms": round(ms_tm, 4), "kv_GBps": round(kv_bytes / (ms_tm * 1e-3) / 1e9, 1),
+                           "frac_hbm": round(kv_bytes / (ms_tm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
            "timing": "median of 50 launches, each after a 512 MiB read that evicts the caches; ms_warm: back-to-back mean"}
-    del d, R, o, ws
+    del d, R, o, keep, kh, vh
     torch.cuda.empty_cache()
     return res
 
@@ -319,14 +351,15 @@ def prologue_leg(rba, torch, name, new_tokens, seq_lens, Skv, reps, mxfp8=False)
     inp = make_prologue_inputs(new_tokens, seq_lens, Hq=64, Hkv=8, W=4)
     d = {k: v.to("cuda") for k, v in inp.items()}
     B, T = len(new_tokens), int(sum(new_tokens))
+    # the decode legs' cache layout: head-major storage behind [B, Skv, Hkv, ...] views
+    def cache(n, dt):
+        return torch.zeros(B, 8, Skv, n, dtype=dt, device="cuda").transpose(1, 2)
+
     if mxfp8:
-        kc = torch.zeros(B, Skv, 8, 128, dtype=torch.uint8, device="cuda")
-        vc = torch.zeros_like(kc)
-        ks = torch.zeros(B, Skv, 8, 4, dtype=torch.uint8, device="cuda")
-        vs = torch.zeros_like(ks)
+        kc, vc = cache(128, torch.uint8), cache(128, torch.uint8)
+        ks, vs = cache(4, torch.uint8), cache(4, torch.uint8)
     else:
-        kc = torch.zeros(B, Skv, 8, 128, dtype=torch.bfloat16, device="cuda")
-        vc = torch.zeros_like(kc)
+        kc, vc = cache(128, torch.bfloat16), cache(128, torch.bfloat16)
         ks = vs = None
     qo = torch.empty_like(d["q"])
     # the call once through the binding (checks), then the C entry point with prebuilt arguments
@@ -350,7 +383,8 @@ def prologue_leg(rba, torch, name, new_tokens, seq_lens, Skv, reps, mxfp8=False)
     nbytes = T * (64 + 16) * row + 2 * B * 3 * 8 * row * 2 + T * 64 * row + T * 16 * kv_row
     res = {"ms": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": nbytes, "tokens": T,
-           "cache": "MXFP8" if mxfp8 else "bf16", "timing": "back-to-back mean after a clock warm-up"}
+           "cache": ("MXFP8" if mxfp8 else "bf16") + ", head-major [B, Hkv, Skv, d] storage",
+           "timing": "back-to-back mean after a clock warm-up"}
     del d, kc, vc, ks, vs, qo
     torch.cuda.empty_cache()
     return res

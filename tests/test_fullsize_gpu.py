@@ -33,12 +33,17 @@ def rows_for(w, n_random, seed):
     return rows
 
 
-def run_and_check(name, decode, n_random, b_subset=None, bias_ratio=0.3):
+def run_and_check(name, decode, n_random, b_subset=None, bias_ratio=0.3, kv_head_major=False):
     import relative_position_bias_rba_amd as rba
     w = CONFIGS[name]
     say(f"[{name}] generating inputs {w}")
     inp = make_inputs(w)
     d = {k: v.to(DEV) for k, v in inp.items()}
+    if kv_head_major:
+        # the same values stored [B, Hkv, Skv, d], passed as a strided view
+        # (the decode benchmark's cache layout)
+        for n in ("k", "v"):
+            d[n] = d[n].transpose(1, 2).contiguous().transpose(1, 2)
     say(f"[{name}] relproj + attention on the GPU")
     R = rba.relproj(d["r"], d["P"])
     if decode:
@@ -93,15 +98,18 @@ def test_c3_full_prefill_fullsize():
     run_and_check("c3_full_prefill", False, 10)
 
 
-def test_c4_decode_swa_fullsize():
-    run_and_check("c4_decode_swa", True, 0, b_subset={0, 17, 63})
+@pytest.mark.parametrize("kv_head_major", [False, True], ids=["token_major", "head_major"])
+def test_c4_decode_swa_fullsize(kv_head_major):
+    run_and_check("c4_decode_swa", True, 0, b_subset={0, 17, 63}, kv_head_major=kv_head_major)
 
 
-def test_c4_decode_full_fullsize():
-    run_and_check("c4_decode_full", True, 0, b_subset={0, 40, 63})
+@pytest.mark.parametrize("kv_head_major", [False, True], ids=["token_major", "head_major"])
+def test_c4_decode_full_fullsize(kv_head_major):
+    run_and_check("c4_decode_full", True, 0, b_subset={0, 40, 63}, kv_head_major=kv_head_major)
 
 
-def test_c5_long_decode_fullsize():
+@pytest.mark.parametrize("kv_head_major", [False, True], ids=["token_major", "head_major"])
+def test_c5_long_decode_fullsize(kv_head_major):
     # 512 biased keys among 262,144: the bias moves o by about as much as
     # bf16 rounding does, so the ratio bound is looser here
-    run_and_check("c5_long_decode", True, 0, bias_ratio=0.6)
+    run_and_check("c5_long_decode", True, 0, bias_ratio=0.6, kv_head_major=kv_head_major)

@@ -61,9 +61,14 @@ def poison(inp, page_size):
     return inp
 
 
-def run_paged(inp, w, page_size, splits, R=None):
+def run_paged(inp, w, page_size, splits, R=None, head_major=False):
+    """head_major: every page stored [Hkv, page_size, d], passed as a strided
+    [page_size, Hkv, d] view."""
     m = rba()
     d = {k: v.to(DEV) for k, v in inp.items()}
+    if head_major:
+        for n in ("k_pool", "v_pool"):
+            d[n] = d[n].transpose(1, 2).contiguous().transpose(1, 2)
     if R is None:
         R = m.relproj(d["r"], d["P"])
     o, lse = m.attn_paged(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"], R,
@@ -105,6 +110,20 @@ def test_paged_parity(name, wname, over, ps, splits):
     fp32 = w.dtype == "fp32"
     check(f"paged {name}/{splits} o", o, wo, fp32)
     check(f"paged {name}/{splits} lse", lse, wl, True, extra_tol=None if fp32 else 2e-2)
+
+
+@pytest.mark.parametrize("name,wname,over,ps", PAGED_CASES[:3], ids=[c[0] for c in PAGED_CASES[:3]])
+def test_paged_head_major_pages(name, wname, over, ps):
+    w = scaled(CONFIGS[wname], **over)
+    say(f"paged head-major {name} page={ps}: {w}")
+    inp = poison(make_paged_inputs(w, ps), ps)
+    for splits in (1, 0):
+        o, lse = run_paged(inp, w, ps, splits, head_major=True)
+        o_tm, lse_tm = run_paged(inp, w, ps, splits)
+        wo, wl = oracle_paged(inp, w)
+        check(f"paged head-major {name}/{splits} o", o, wo, False)
+        check(f"paged head-major {name}/{splits} lse", lse, wl, True, extra_tol=2e-2)
+        assert torch.equal(o, o_tm) and torch.equal(lse, lse_tm)
 
 
 def test_paged_lengths_at_both_ends():

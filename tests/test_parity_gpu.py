@@ -185,9 +185,16 @@ def test_calibration_kernels_run():
 
 # --------------------------------------------------------------------------- prefill, small shapes, every element
 
-def run_path(inp, w, *, decode=False, splits=0, return_lse=True):
+def head_major(x):
+    """The same [B, S, H, d] values stored head-major ([B, H, S, d]), as a view."""
+    return x.transpose(1, 2).contiguous().transpose(1, 2)
+
+
+def run_path(inp, w, *, decode=False, splits=0, return_lse=True, kv_head_major=False):
     m = rba()
     d = to_dev(inp)
+    if kv_head_major:
+        d["k"], d["v"] = head_major(d["k"]), head_major(d["v"])
     R = m.relproj(d["r"], d["P"])
     fn = m.attn_decode if decode else m.attn_prefill
     kw = dict(window=w.window, log_scale_base=w.log_scale_base, return_lse=return_lse)
@@ -392,6 +399,23 @@ def test_decode_small(name, over, splits):
     wo, wl = oracle_full(inp, w)
     check(f"decode {name}/{splits} o", o, wo, False)
     check(f"decode {name}/{splits} lse", lse, wl, True, extra_tol=2e-2)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 0])
+@pytest.mark.parametrize("name,over", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_small_head_major_cache(name, over, splits):
+    # the cache stored [B, Hkv, Skv, d] and passed with its strides: every key
+    # tile of a kv head is one contiguous block
+    w = small(CONFIGS["c4_decode_full"], Hq=16, Hkv=2, E=64, **over)
+    say(f"decode head-major {name} splits={splits}: {w}")
+    inp = make_inputs(w)
+    o, lse = run_path(inp, w, decode=True, splits=splits, kv_head_major=True)
+    o_tm, lse_tm = run_path(inp, w, decode=True, splits=splits)
+    wo, wl = oracle_full(inp, w)
+    check(f"decode head-major {name}/{splits} o", o, wo, False)
+    check(f"decode head-major {name}/{splits} lse", lse, wl, True, extra_tol=2e-2)
+    # the layout changes addresses only
+    assert torch.equal(o, o_tm) and torch.equal(lse, lse_tm)
 
 
 def test_decode_split_invariance_and_prefill_agreement():

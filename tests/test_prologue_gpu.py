@@ -42,14 +42,22 @@ def close(name, got, want):
     assert not bad.any(), f"{name}: {bad.sum()} entries off, first {np.argwhere(bad)[:3].tolist()}"
 
 
-def run(inp, Skv, *, f8=False, paged=None, W=None):
+def run(inp, Skv, *, f8=False, paged=None, W=None, head_major=False):
+    """head_major: the dense cache is stored [B, Hkv, Skv, ...] and passed as a
+    [B, Skv, Hkv, ...] view with those strides."""
     m = rba()
     d = {k: v.to(DEV) for k, v in inp.items()}
     B = d["seq_lens"].shape[0]
     Hkv = d["k"].shape[1]
+
+    def cache(shape, fill, dtype):
+        if not head_major:
+            return torch.full(shape, fill, dtype=dtype, device=DEV)
+        return torch.full((shape[0], shape[2], shape[1], shape[3]), fill, dtype=dtype, device=DEV).transpose(1, 2)
+
     if paged is None:
-        kc = torch.full((B, Skv, Hkv, 128), SENTINEL, dtype=torch.bfloat16, device=DEV)
-        vc = torch.full_like(kc, -SENTINEL)
+        kc = cache((B, Skv, Hkv, 128), SENTINEL, torch.bfloat16)
+        vc = cache((B, Skv, Hkv, 128), -SENTINEL, torch.bfloat16)
         table = None
     else:
         ps, n_pages, table = paged
@@ -58,10 +66,10 @@ def run(inp, Skv, *, f8=False, paged=None, W=None):
         table = table.to(DEV)
     ks = vs = None
     if f8:
-        kc = torch.full(kc.shape, 0x55, dtype=torch.uint8, device=DEV)
-        vc = torch.full(vc.shape, 0x66, dtype=torch.uint8, device=DEV)
-        ks = torch.full((*kc.shape[:3], 4), 0x11, dtype=torch.uint8, device=DEV)
-        vs = torch.full_like(ks, 0x22)
+        kc = cache(tuple(kc.shape), 0x55, torch.uint8)
+        vc = cache(tuple(vc.shape), 0x66, torch.uint8)
+        ks = cache((*kc.shape[:3], 4), 0x11, torch.uint8)
+        vs = cache((*kc.shape[:3], 4), 0x22, torch.uint8)
     sk, sv = d["state_k"].clone(), d["state_v"].clone()
     qo = m.attn_prologue(d["q"], d["k"], d["v"], d["cu_new"], d["seq_lens"], d["conv_wk"], d["conv_wv"],
                          d["norm_q"], d["norm_k"], sk if sk.numel() else None, sv if sv.numel() else None, kc, vc,
@@ -102,6 +110,20 @@ def test_prologue_dense_bf16(W):
     assert torch.all(kc[mask.to(DEV)] == SENTINEL) and torch.all(vc[mask.to(DEV)] == -SENTINEL)
     if W > 1:
         assert np.array_equal(sk.double().cpu().numpy(), nsk) and np.array_equal(sv.double().cpu().numpy(), nsv)
+
+
+@pytest.mark.parametrize("f8", [False, True], ids=["bf16", "mxfp8"])
+def test_prologue_head_major_cache(f8):
+    # the dense cache stored head-major: the same rows land at the strided
+    # addresses, every other entry keeps its fill
+    say(f"prologue head-major cache f8={f8}")
+    inp = make_prologue_inputs(MIX["new"], MIX["lens"], Hq=16, Hkv=2, W=4, seed=23)
+    got = run(inp, 512, f8=f8, head_major=True)
+    ref = run(inp, 512, f8=f8)
+    assert not got[1].is_contiguous() and ref[1].is_contiguous()
+    for g, r in zip(got, ref):
+        if r is not None:
+            assert torch.equal(g, r)
 
 
 def test_prologue_two_calls_carry_the_state():
