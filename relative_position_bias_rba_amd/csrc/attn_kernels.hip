@@ -666,7 +666,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         const bool band = banded(kt);
         const bool edge = !((j0 + N - 1 <= p_min) && (W == 0 || p_max - j0 < W));
 
-        float mt = -INFINITY;
         if (band) {
             // x = scale f q.k + f bias, in log2 units
             const T *sr = &sR[sbuf][s_lane];
@@ -684,74 +683,77 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
                     if (partial) bias = (32 * u + r > elim) ? bias : 0.f;
                     S[u][r] = fmaf(bias, bmul, S[u][r] * amul);
                 }
-            if (edge) {
-#pragma unroll
-                for (int u = 0; u < KT; ++u)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int dist = prow - (j0 + 32 * u + 16 * hh + r);
-                        const bool vis = dist >= 0 && (W == 0 || dist < W);
-                        S[u][r] = vis ? S[u][r] : -INFINITY;
-                    }
-            }
+        }
+        if (edge) {
 #pragma unroll
             for (int u = 0; u < KT; ++u)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, S[u][r]);
-        } else {
-            // raw dot products; the scale is applied inside the exponent
-            if (edge) {
-#pragma unroll
-                for (int u = 0; u < KT; ++u)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int dist = prow - (j0 + 32 * u + 16 * hh + r);
-                        const bool vis = dist >= 0 && (W == 0 || dist < W);
-                        S[u][r] = vis ? S[u][r] : -INFINITY;
-                    }
-            }
-#pragma unroll
-            for (int u = 0; u < KT; ++u)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, S[u][r]);
-            mt *= amul;
+                for (int r = 0; r < 16; ++r) {
+                    const int dist = prow - (j0 + 32 * u + 16 * hh + r);
+                    const bool vis = dist >= 0 && (W == 0 || dist < W);
+                    S[u][r] = vis ? S[u][r] : -INFINITY;
+                }
         }
+        // multiplier still to apply to S (interior tiles hold raw dot products)
+        const float sa = band ? 1.f : amul;
 
-        // online softmax (exp2 domain).  The reference max only moves when the
-        // tile max exceeds it by more than kRescaleSlack; O and l are rescaled
-        // only when some lane of the wave moves it.  Exact: numerator and
-        // denominator always share the reference.
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const bool grow = mt > m + kRescaleSlack;
-        if (__ballot(grow) != 0) {
-            const float mn = grow ? mt : m;
-            const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
-            m = mn;
-            l *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) O[dt] *= alpha;
-        }
-        const float mu = m == -INFINITY ? 0.f : m;
-        const float sa = band ? 1.f : amul;     // multiplier still to apply to S
-#pragma unroll
-        for (int u = 0; u < KT; ++u)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S[u][r] = fast_exp2(fmaf(S[u][r], sa, -mu));
-
-        // O^T += V^T . P^T ; the row sum uses the same rounded P as the product
         if constexpr (BF) {
+            // Probabilities against the current reference max m (exp2 domain),
+            // rounded to bf16 for PV; the row sum adds the fp32 values in two
+            // chains (a v_dot2c sum over the bf16 values stalls beside the
+            // other workgroup's MFMAs on the same SIMD).  The reference only
+            // moves when the tile max exceeds it by more than kRescaleSlack.
+            // While this lane's probabilities sum to at most 2^kRescaleSlack
+            // none of them exceeds that bound, so the tile max is not needed;
+            // otherwise, and at a column's first visible tile, it is taken and,
+            // if m moves, O and l are rescaled and P recomputed.  Decisions
+            // are wave-uniform, so both halves of a column decide alike.
+            bf16x8 P[2 * KT];
             float sum = 0.f;
+            auto exps = [&](float mu) __attribute__((always_inline)) {
+                float sm[2] = {0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < KT; ++u)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        bf16x8 pb;
+#pragma unroll
+                        for (int x = 0; x < 8; ++x) {
+                            const float e = fast_exp2(fmaf(S[u][8 * h2 + x], sa, -mu));
+                            pb[x] = (__bf16)e;
+                            sm[x & 1] += e;
+                        }
+                        P[2 * u + h2] = pb;
+                    }
+                sum = sm[0] + sm[1];
+            };
+            exps(m == -INFINITY ? 0.f : m);
+            const bool slow = !(sum <= kRescaleLimit) || m == -INFINITY;
+            if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+                float mt = -INFINITY;
+#pragma unroll
+                for (int u = 0; u < KT; ++u)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, S[u][r]);
+                mt = max_across_halves(mt * sa);
+                const bool grow = mt > m + kRescaleSlack;
+                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                    const float mn = grow ? mt : m;
+                    const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+                    m = mn;
+                    l *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) O[dt] *= alpha;
+                    exps(m == -INFINITY ? 0.f : m);
+                }
+            }
+            l += sum;
+
+            // O^T += V^T . P^T
 #pragma unroll
             for (int u = 0; u < KT; ++u) {
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
-                    bf16x8 pb;
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) pb[x] = (__bf16)S[u][8 * h2 + x];
-#pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        sum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[2 * x], pb[2 * x + 1]},
-                                                              bf16x2{(__bf16)1.f, (__bf16)1.f}, sum, false);
 #pragma unroll
                     for (int dt = 0; dt < 4; ++dt) {
                         bf16x8 a;
@@ -766,12 +768,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
                         } else {
                             a = *(const bf16x8 *)(v_lane + 32 * dt * VS + 32 * u + 8 * h2);
                         }
-                        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, O[dt], 0, 0, 0);
+                        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[2 * u + h2], O[dt], 0, 0, 0);
                     }
                 }
             }
-            l += sum;
         } else {
+            // fp32: max first, then the exponentials in place
+            float mt = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, S[0][r]);
+            mt = max_across_halves(mt * sa);
+            const bool grow = mt > m + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                const float mn = grow ? mt : m;
+                const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+                m = mn;
+                l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) O[dt] *= alpha;
+            }
+            const float mu = m == -INFINITY ? 0.f : m;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[0][r] = fast_exp2(fmaf(S[0][r], sa, -mu));
             float sum = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
