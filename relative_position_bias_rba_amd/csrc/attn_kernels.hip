@@ -216,16 +216,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     constexpr int KCH = N * CPRP;                // K chunks per tile incl. padding
     constexpr int NKI = (KCH + NTH - 1) / NTH;   // K DMA instructions per thread
     constexpr int NVI = BF ? N * D / (NTH * 4) : N * CPR / NTH;  // V loads per thread
-    constexpr int NSB = (SLAB2 || F8) ? 2 : 1;
     static_assert(NVI * NTH * (BF ? 4 : CH) == N * D, "V tile must split evenly over threads");
 
-    // F8: one K and one V buffer (registers carry the tiles in flight); V is
-    // row-major with 16-byte chunks XOR-swizzled by row and read transposed
-    constexpr int NKB = F8 ? 1 : 2;
+    // FQ: K stays MXFP8 in LDS: row r of codes at byte K8R * r (DMA chunk
+    // 8 of a row repeats chunk 0), the four scale bytes of row r at K8S + 4 r.
+    constexpr int K8R = D + 16;                 // padded code row (bytes)
+    constexpr int K8S = N * K8R;
+    // FQ2 (MXFP8 logits, 4 waves): K codes and decoded V in two buffers each,
+    // one bias buffer; the next tile's V is decoded right after this tile's
+    // compute, so a tile takes one barrier.
+    constexpr bool FQ2 = FQ && NW == 4;
+    // F8 otherwise: one K and one V buffer (registers carry the tiles in
+    // flight).  V is row-major with 16-byte chunks XOR-swizzled by row and
+    // read transposed.
+    constexpr int NKB = F8 ? (FQ2 ? 2 : 1) : 2;
+    constexpr int KBE = FQ2 ? (K8S + 4 * N) / (int)sizeof(T) : N * KS;   // elements of one K buffer
+    constexpr int NVB = FQ2 ? 2 : 1;
     constexpr int VSZ = F8 ? N * D : TL::VROWS * VS;
-    __shared__ __attribute__((aligned(16))) T sK[NKB][N * KS];
-    __shared__ __attribute__((aligned(16))) T sV[VSZ];
+    constexpr int NSB = FQ2 ? 1 : ((SLAB2 || F8) ? 2 : 1);
+    __shared__ __attribute__((aligned(16))) T sK[NKB][KBE];
+    __shared__ __attribute__((aligned(16))) T sV[NVB * VSZ];
     __shared__ __attribute__((aligned(16))) T sR[NSB][SROWS * SW];
+    static_assert(!FQ || K8S + 4 * N <= KBE * (int)sizeof(T), "K codes and scales fit a K buffer");
+    constexpr int KBB = KBE * (int)sizeof(T);   // bytes of one K buffer
+    unsigned char *const sK8 = (unsigned char *)&sK[0][0];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -427,7 +441,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     constexpr int NP8 = F8 ? N * D / 16 / NTH : 1;
     struct F8Set {
         u32x4 k[NP8], v[NP8];
-        unsigned ks[NP8], vs[NP8];
+        unsigned char ks[NP8], vs[NP8];   // E8M0 codes, widened where used
     };
     // Offsets of piece 0; piece i is NTH / 8 rows further (the row
     // permutation and the chunk swizzle do not change over 32 rows).
@@ -465,6 +479,46 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         }
     };
 
+    // The same rows as descriptor words, for dma16_untracked.
+    auto kv_rsrc_words = [&](const char *g, int64_t pstride, int64_t stride, int j0, int esz, int rowbytes) {
+        if constexpr (PG) {
+            const int pg = __builtin_amdgcn_readfirstlane(j0 / p.page_size);
+            const int off = j0 - pg * p.page_size;
+            const int page = min(max(load_scalar(p.block_table + (int64_t)b * p.bt_stride + pg), 0), p.num_pages - 1);
+            const int rows = min(p.page_size - off, Skv - j0);
+            return make_rsrc_words(g + ((int64_t)page * pstride + (int64_t)off * stride) * esz,
+                                   (int64_t)(rows - 1) * stride * esz + rowbytes);
+        } else {
+            return make_rsrc_words(g + (int64_t)j0 * stride * esz, (int64_t)(Skv - 1 - j0) * stride * esz + rowbytes);
+        }
+    };
+
+    // FQ2: K codes of tile kt into K buffer buf by direct-to-LDS loads: LDS
+    // chunk L (16 bytes) holds chunk L % 9 of code row L / 9, the ninth
+    // (padding) chunk a repeat of chunk 0.  Untracked: the caller's counted
+    // wait lands them before the barrier that hands them over.
+    constexpr int K8CH = N * (K8R / 16);                 // 576 chunks
+    constexpr int NK8I = (K8CH + NTH - 1) / NTH;
+    unsigned k8vo[FQ2 ? NK8I : 1] = {};
+    if constexpr (FQ2) {
+#pragma unroll
+        for (int i = 0; i < NK8I; ++i) {
+            const int L = (i * NW + wave) * 64 + lane;
+            const int row = L / (K8R / 16), c = L - row * (K8R / 16);
+            k8vo[i] = (unsigned)((int64_t)min(row, N - 1) * p.ks1 + 16 * (c < D / 16 ? c : 0));
+        }
+    }
+    auto stage_k8 = [&](int kt, int buf) __attribute__((always_inline)) {
+        if constexpr (FQ2) {
+            const u32x4 rk = kv_rsrc_words(gk, p.ks0, p.ks1, kt * N, 1, D);
+#pragma unroll
+            for (int i = 0; i < NK8I; ++i) {
+                const int wc = (i * NW + wave) * 64;        // wave-uniform: whole waves in or out
+                if (wc < K8CH) dma16_untracked(rk, k8vo[i], sK8 + buf * KBB + wc * 16);
+            }
+        }
+    };
+
     // F8: codes and scales of tile kt's K and V into register set X
     auto load8 = [&](int kt, F8Set &X) __attribute__((always_inline)) {
         const rsrc_t rk = kv_rsrc(gk, p.ks0, p.ks1, kt * N, 1, D);
@@ -474,31 +528,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 #pragma unroll
         for (int i = 0; i < NP8; ++i) {
             const unsigned r = (unsigned)(i * RSTEP);
-            X.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k8o + r * (unsigned)p.ks1, 0, 0);
+            if constexpr (!FQ2) X.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k8o + r * (unsigned)p.ks1, 0, 0);
             X.ks[i] = __builtin_amdgcn_raw_buffer_load_b8(rks, k8s + r * (unsigned)p.kss1, 0, 0);
             X.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v8o + r * (unsigned)p.vs1, 0, 0);
             X.vs[i] = __builtin_amdgcn_raw_buffer_load_b8(rvs, v8s + r * (unsigned)p.vss1, 0, 0);
         }
     };
-    // vector-memory instructions one load8 issues
-    constexpr int kLoad8Ops = 4 * NP8;
-
-    // FQ: K stays MXFP8 in LDS: row r of codes at byte K8R * r, the four
-    // scale bytes of row r at K8S + 4 r.
-    constexpr int K8R = D + 16;                 // padded code row (bytes)
-    constexpr int K8S = N * K8R;
-    static_assert(!FQ || K8S + 4 * N <= (int)sizeof(sK), "K codes and scales fit the K buffer");
-    unsigned char *const sK8 = (unsigned char *)&sK[0][0];
+    // vector-memory instructions one load8 issues (FQ2: K codes go by DMA)
+    constexpr int kLoad8Ops = (FQ2 ? 3 : 4) * NP8;
 
     // F8: decode register set X into the K and V buffers (bf16)
-    auto store8 = [&](const F8Set &X) __attribute__((always_inline)) {
+    auto store8 = [&](const F8Set &X, int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NP8; ++i) {
             const float sk = e8m0_scale(X.ks[i]), sv = e8m0_scale(X.vs[i]);
             if constexpr (FQ) {
                 const int row = (tid >> 3) + i * RSTEP, c = tid & 7;
-                *(u32x4 *)&sK8[row * K8R + 16 * c] = X.k[i];
-                if ((c & 1) == 0) sK8[K8S + 4 * row + (c >> 1)] = (unsigned char)X.ks[i];
+                if constexpr (!FQ2) *(u32x4 *)&sK8[row * K8R + 16 * c] = X.k[i];
+                if ((c & 1) == 0) sK8[buf * KBB + K8S + 4 * row + (c >> 1)] = (unsigned char)X.ks[i];
             } else {
                 u32x2 a = e4m3x4_to_bf16(X.k[i][0], sk), b2 = e4m3x4_to_bf16(X.k[i][1], sk);
                 u32x2 c = e4m3x4_to_bf16(X.k[i][2], sk), d = e4m3x4_to_bf16(X.k[i][3], sk);
@@ -508,7 +555,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
             }
             u32x2 a = e4m3x4_to_bf16(X.v[i][0], sv), b2 = e4m3x4_to_bf16(X.v[i][1], sv);
             u32x2 c = e4m3x4_to_bf16(X.v[i][2], sv), d = e4m3x4_to_bf16(X.v[i][3], sv);
-            T *dst = &sV[v8d + i * RSTEP * D];
+            T *dst = &sV[buf * VSZ + v8d + i * RSTEP * D];
             *(u32x4 *)dst = u32x4{a[0], a[1], b2[0], b2[1]};
             *(u32x4 *)(dst + 8) = u32x4{c[0], c[1], d[0], d[1]};
         }
@@ -636,11 +683,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 #pragma unroll
                 for (int u = 0; u < KT; ++u) {
                     const int kr = 32 * u + mfma_row_key(lc);
-                    const unsigned char *src = sK8 + kr * K8R + 64 * ks + 16 * hh;
+                    const unsigned char *src = sK8 + buf * KBB + kr * K8R + 64 * ks + 16 * hh;
                     const u32x4 lo = *(const u32x4 *)src, hi = *(const u32x4 *)(src + 32);
                     const i32x8 a = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                    const int sa = sK8[K8S + 4 * kr + 2 * ks + hh];
+                    const int sa = sK8[buf * KBB + K8S + 4 * kr + 2 * ks + hh];
                     S[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q8[ks], S[u], 0, 0, 0, sa, 0, qsc[ks]);
                 }
             }
@@ -759,7 +806,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
                         bf16x8 a;
                         if constexpr (F8) {
                             typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-                            const T *base = &sV[vt_off(dt) + (32 * u + 8 * h2) * D];
+                            const T *base = &sV[(FQ2 ? buf * VSZ : 0) + vt_off(dt) + (32 * u + 8 * h2) * D];
                             const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                                 (__attribute__((address_space(3))) bf16x4_t *)base);
                             const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -847,7 +894,56 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         }
     };
     int kt = n_it > 0 ? next_tile() : 0;
-    if constexpr (F8) {
+    if constexpr (FQ2) {
+        // K codes by DMA one tile ahead into alternating buffers; V codes and
+        // the scales of both two tiles ahead through the register sets.  Right
+        // after computing tile kt each thread decodes its share of the next
+        // tile into the other buffers, and one barrier per tile hands both
+        // over.  The single bias buffer is loaded ahead when the tile being
+        // computed carries no bias, else after the barrier (then a second one).
+        F8Set A, B;
+        int kn = n_it > 1 ? next_tile() : kt;
+        if (n_it > 0) {
+            stage_k8(kt, 0);
+            load8(kt, A);
+            load8(kn, B);
+            if (banded(kt)) stage_slab(kt, 0);
+            store8(A, 0);
+            wait_vmem();
+        }
+        __syncthreads();
+        auto body = [&](int it, F8Set &X, F8Set &Y) __attribute__((always_inline)) {
+            fair_prio(it);
+            const int cur = it & 1;
+            const bool nxt = it + 1 < n_it, nxt2 = it + 2 < n_it;
+            const int kn2 = nxt2 ? next_tile() : kn;
+            const bool sahead = nxt && r_dma && banded(kn) && !banded(kt);
+            if (nxt) stage_k8(kn, cur ^ 1);           // last read by the previous tile's compute
+            if (sahead) stage_slab_ahead(kn, 0);
+            // Issued on every tile (the last two repeat a tile and are never
+            // stored), so that the compiler's wait for X before the stores
+            // below counts Y's loads on every path and leaves them in flight.
+            load8(kn2, Y);
+            if (wave_active) compute_tile(kt, cur, 0);
+            if (nxt) store8(X, cur ^ 1);
+            // K codes and bias of kn landed (issued before Y's loads)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoad8Ops) : "memory");
+            __syncthreads();
+            if (nxt && banded(kn) && !sahead) {
+                stage_slab(kn, 0);
+                wait_vmem();
+                __syncthreads();
+            }
+            kt = kn;
+            kn = kn2;
+        };
+        for (int it = 0; it < n_it; it += 2) {
+            body(it, B, A);
+            if (it + 1 < n_it) body(it + 1, A, B);
+        }
+        wait_vmem();
+    }
+    if constexpr (F8 && !FQ2) {
         // Two tiles in flight: while tile kt is computed from LDS, the codes of
         // tile kn wait in one register set and those of the tile after it load
         // into the other; each iteration decodes kn into the (single) K and V
@@ -860,7 +956,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
             load8(kt, A);
             if (n_it > 1) load8(kn, B);
             if (banded(kt)) stage_slab(kt, 0);
-            store8(A);
+            store8(A, 0);
             wait_vmem();
         }
         __syncthreads();
@@ -881,7 +977,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
             }
             __syncthreads();                             // kt consumed; kn's bias landed
             if (nxt) {
-                store8(X);
+                store8(X, 0);
                 if (!r_dma && banded(kn)) {
                     stage_slab(kn, sb ^ 1);
                     wait_vmem();
