@@ -561,6 +561,45 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         }
     };
 
+    // FQ2 with a wave that has no columns: that wave alone moves V and the
+    // scales of a tile through its registers (8 pieces a lane: piece i of
+    // lane l is row 8 i + l / 8, 16-code piece l % 8) and decodes them, while
+    // the other waves compute.
+    struct F8SetP {
+        u32x4 v[8];
+        unsigned char ks[8], vs[8];
+    };
+    const int pc8 = lane & 7, pr8 = lane >> 3;
+    const unsigned k8sP = (unsigned)((int64_t)pr8 * p.kss1 + (pc8 >> 1));
+    const unsigned v8oP = (unsigned)((int64_t)pr8 * p.vs1 + 16 * pc8);
+    const unsigned v8sP = (unsigned)((int64_t)pr8 * p.vss1 + (pc8 >> 1));
+    auto load8P = [&](int kt, F8SetP &X) __attribute__((always_inline)) {
+        const rsrc_t rks = kv_rsrc(gks, p.kss0, p.kss1, kt * N, 1, D / 32);
+        const rsrc_t rv = kv_rsrc(gv, p.vs0, p.vs1, kt * N, 1, D);
+        const rsrc_t rvs = kv_rsrc(gvs, p.vss0, p.vss1, kt * N, 1, D / 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const unsigned r = (unsigned)(8 * i);
+            X.ks[i] = __builtin_amdgcn_raw_buffer_load_b8(rks, k8sP + r * (unsigned)p.kss1, 0, 0);
+            X.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v8oP + r * (unsigned)p.vs1, 0, 0);
+            X.vs[i] = __builtin_amdgcn_raw_buffer_load_b8(rvs, v8sP + r * (unsigned)p.vss1, 0, 0);
+        }
+    };
+    constexpr int kLoad8POps = 24;   // vector-memory instructions one load8P issues
+    auto store8P = [&](const F8SetP &X, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 8 * i + pr8;
+            if ((pc8 & 1) == 0) sK8[buf * KBB + K8S + 4 * row + (pc8 >> 1)] = X.ks[i];
+            const float sv = e8m0_scale(X.vs[i]);
+            const u32x2 a = e4m3x4_to_bf16(X.v[i][0], sv), b2 = e4m3x4_to_bf16(X.v[i][1], sv);
+            const u32x2 c = e4m3x4_to_bf16(X.v[i][2], sv), d = e4m3x4_to_bf16(X.v[i][3], sv);
+            T *dst = &sV[buf * VSZ + row * D + 8 * ((2 * pc8) ^ ((row & 3) << 2))];
+            *(u32x4 *)dst = u32x4{a[0], a[1], b2[0], b2[1]};
+            *(u32x4 *)(dst + 8) = u32x4{c[0], c[1], d[0], d[1]};
+        }
+    };
+
     auto stage_k = [&](int kt, int buf) {
         const rsrc_t rk = kv_rsrc(gk, p.ks0, p.ks1, kt * N, ES, D * ES);
 #pragma unroll
@@ -666,7 +705,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     auto vt_off = [&](int dt) __attribute__((always_inline)) { return vt_base + CH * (((dt ^ tr_i) << 2)); };
     const int s_lane = col * SW + (prow - rb) - 16 * hh;   // slab entry of key offset 16*hh
 
-    auto compute_tile = [&](int kt, int buf, int sbuf) {
+    auto compute_tile = [&](int kt, int buf, int sbuf) __attribute__((always_inline)) {
         const int j0 = kt * N;
         f32x16 S[KT];
 #pragma unroll
@@ -896,38 +935,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     int kt = n_it > 0 ? next_tile() : 0;
     if constexpr (FQ2) {
         // K codes by DMA one tile ahead into alternating buffers; V codes and
-        // the scales of both two tiles ahead through the register sets.  Right
-        // after computing tile kt each thread decodes its share of the next
-        // tile into the other buffers, and one barrier per tile hands both
-        // over.  The single bias buffer is loaded ahead when the tile being
-        // computed carries no bias, else after the barrier (then a second one).
-        F8Set A, B;
+        // the scales of both two tiles ahead through registers.  The next
+        // tile's V is decoded into the other buffers while this tile is
+        // computed, and one barrier per tile hands both over.  With a wave
+        // that has no columns, that wave (the last) does all of the decoding;
+        // otherwise every thread decodes its share right after its compute.
+        // The single bias buffer is loaded ahead when the tile being computed
+        // carries no bias, else after the barrier (then a second one).
+        const bool split = (NW - 1) * 32 >= ncols;          // the last wave has no columns
+        const bool producer = split && wave == NW - 1;
         int kn = n_it > 1 ? next_tile() : kt;
-        if (n_it > 0) {
-            stage_k8(kt, 0);
-            load8(kt, A);
-            load8(kn, B);
-            if (banded(kt)) stage_slab(kt, 0);
-            store8(A, 0);
-            wait_vmem();
-        }
-        __syncthreads();
-        auto body = [&](int it, F8Set &X, F8Set &Y) __attribute__((always_inline)) {
-            fair_prio(it);
-            const int cur = it & 1;
-            const bool nxt = it + 1 < n_it, nxt2 = it + 2 < n_it;
-            const int kn2 = nxt2 ? next_tile() : kn;
-            const bool sahead = nxt && r_dma && banded(kn) && !banded(kt);
-            if (nxt) stage_k8(kn, cur ^ 1);           // last read by the previous tile's compute
-            if (sahead) stage_slab_ahead(kn, 0);
-            // Issued on every tile (the last two repeat a tile and are never
-            // stored), so that the compiler's wait for X before the stores
-            // below counts Y's loads on every path and leaves them in flight.
-            load8(kn2, Y);
-            if (wave_active) compute_tile(kt, cur, 0);
-            if (nxt) store8(X, cur ^ 1);
-            // K codes and bias of kn landed (issued before Y's loads)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoad8Ops) : "memory");
+        // the barriers of one tile, common to both roles; returns kn's successor
+        auto tile_end = [&](int it, bool sahead, int kn2) __attribute__((always_inline)) {
+            const bool nxt = it + 1 < n_it;
             __syncthreads();
             if (nxt && banded(kn) && !sahead) {
                 stage_slab(kn, 0);
@@ -937,11 +957,87 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
             kt = kn;
             kn = kn2;
         };
-        for (int it = 0; it < n_it; it += 2) {
-            body(it, B, A);
-            if (it + 1 < n_it) body(it + 1, A, B);
+        auto tile_begin = [&](int it, bool &sahead) __attribute__((always_inline)) {
+            fair_prio(it);
+            const bool nxt = it + 1 < n_it, nxt2 = it + 2 < n_it;
+            const int kn2 = nxt2 ? next_tile() : kn;
+            sahead = nxt && r_dma && banded(kn) && !banded(kt);
+            if (nxt) stage_k8(kn, (it & 1) ^ 1);        // last read by the previous tile's compute
+            if (sahead) stage_slab_ahead(kn, 0);
+            return kn2;
+        };
+        if (split) {
+            if (producer) {
+                F8SetP A, B;
+                if (n_it > 0) {
+                    stage_k8(kt, 0);
+                    load8P(kt, A);
+                    load8P(kn, B);
+                    if (banded(kt)) stage_slab(kt, 0);
+                    store8P(A, 0);
+                    wait_vmem();
+                }
+                __syncthreads();
+                auto body = [&](int it, F8SetP &X, F8SetP &Y) __attribute__((always_inline)) {
+                    bool sahead;
+                    const int kn2 = tile_begin(it, sahead);
+                    // issued on every tile (the last two repeat a tile and are
+                    // never stored), so that every path carries the same count
+                    load8P(kn2, Y);
+                    if (it + 1 < n_it) store8P(X, (it & 1) ^ 1);
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoad8POps) : "memory");
+                    tile_end(it, sahead, kn2);
+                };
+                for (int it = 0; it < n_it; it += 2) {
+                    body(it, B, A);
+                    if (it + 1 < n_it) body(it + 1, A, B);
+                }
+                wait_vmem();
+            } else {
+                if (n_it > 0) {
+                    stage_k8(kt, 0);
+                    if (banded(kt)) stage_slab(kt, 0);
+                    wait_vmem();
+                }
+                __syncthreads();
+                for (int it = 0; it < n_it; ++it) {
+                    bool sahead;
+                    const int kn2 = tile_begin(it, sahead);
+                    if (wave_active) compute_tile(kt, it & 1, 0);
+                    wait_vmem();
+                    tile_end(it, sahead, kn2);
+                }
+            }
+        } else {
+            F8Set A, B;
+            if (n_it > 0) {
+                stage_k8(kt, 0);
+                load8(kt, A);
+                load8(kn, B);
+                if (banded(kt)) stage_slab(kt, 0);
+                store8(A, 0);
+                wait_vmem();
+            }
+            __syncthreads();
+            auto body = [&](int it, F8Set &X, F8Set &Y) __attribute__((always_inline)) {
+                bool sahead;
+                const int kn2 = tile_begin(it, sahead);
+                // issued on every tile (the last two repeat a tile and are never
+                // stored), so that the compiler's wait for X before the stores
+                // below counts Y's loads on every path and leaves them in flight
+                load8(kn2, Y);
+                if (wave_active) compute_tile(kt, it & 1, 0);
+                if (it + 1 < n_it) store8(X, (it & 1) ^ 1);
+                // K codes and bias of kn landed (issued before Y's loads)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoad8Ops) : "memory");
+                tile_end(it, sahead, kn2);
+            };
+            for (int it = 0; it < n_it; it += 2) {
+                body(it, B, A);
+                if (it + 1 < n_it) body(it + 1, A, B);
+            }
+            wait_vmem();
         }
-        wait_vmem();
     }
     if constexpr (F8 && !FQ2) {
         // Two tiles in flight: while tile kt is computed from LDS, the codes of
