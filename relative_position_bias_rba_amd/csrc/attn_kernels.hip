@@ -192,12 +192,16 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16(unsigned w, float sc) {
 // cache's rule (blocks of 32 along d), K stays as codes and scales in LDS,
 // and S^T = K . Q^T runs on v_mfma_scale_f32_32x32x64_f8f6f4, which applies
 // the E8M0 scales of both operands itself; V is decoded for PV as with F8.
-template <typename T, int NW, bool SLAB2, bool PG, bool F8, bool FQ = false>
+// VD (bf16, 4 waves, at most 96 query columns): V goes global -> LDS by
+// direct-to-LDS loads like K, row-major and double-buffered, and is read
+// transposed; no register staging, one barrier per tile.
+template <typename T, int NW, bool SLAB2, bool PG, bool F8, bool FQ = false, bool VD = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnParams p) {
     using TL = Tile<T>;
     constexpr bool BF = sizeof(T) == 2;
     static_assert(!F8 || BF, "MXFP8 K/V is decoded to bf16");
     static_assert(!FQ || F8, "MXFP8 logits need an MXFP8 cache");
+    static_assert(!VD || (BF && !F8 && NW == 4 && !SLAB2), "VD is the 4-wave bf16 decode");
     constexpr int ES = (int)sizeof(T);
     constexpr int KES = F8 ? 1 : ES;             // bytes per K/V element in memory
     constexpr int NTH = 64 * NW;                 // threads per workgroup
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     constexpr int VS = TL::VS;
     constexpr int SW = TL::SW;
     constexpr int NCH = SW / CH;                 // chunks per slab row
-    constexpr int SROWS = NW * 32;               // slab rows = max columns per workgroup
+    constexpr int SROWS = VD ? 96 : NW * 32;     // slab rows = max columns per workgroup
     constexpr int SCH = SROWS * NCH;             // slab chunks
     constexpr int NSI = (SCH + NTH - 1) / NTH;   // slab DMA instructions per thread
     constexpr int CPR = D * ES / 16;             // 16-byte chunks per K/V row
@@ -231,8 +235,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     // read transposed.
     constexpr int NKB = F8 ? (FQ2 ? 2 : 1) : 2;
     constexpr int KBE = FQ2 ? (K8S + 4 * N) / (int)sizeof(T) : N * KS;   // elements of one K buffer
-    constexpr int NVB = FQ2 ? 2 : 1;
-    constexpr int VSZ = F8 ? N * D : TL::VROWS * VS;
+    constexpr int NVB = (FQ2 || VD) ? 2 : 1;
+    constexpr int VSZ = (F8 || VD) ? N * D : TL::VROWS * VS;
     constexpr int NSB = FQ2 ? 1 : ((SLAB2 || F8) ? 2 : 1);
     __shared__ __attribute__((aligned(16))) T sK[NKB][KBE];
     __shared__ __attribute__((aligned(16))) T sV[NVB * VSZ];
@@ -600,12 +604,39 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         }
     };
 
+    // VD: V tile kt into V buffer buf.  LDS chunk L (16 bytes) holds chunk
+    // (L % 16) ^ 4 (r % 4) of key row r = L / 16, the layout the transposed
+    // reads of PV expect.
+    constexpr int NVDI = N * D * ES / 16 / NTH;
+    unsigned vdo[VD ? NVDI : 1] = {};
+    if constexpr (VD) {
+#pragma unroll
+        for (int i = 0; i < NVDI; ++i) {
+            const int L = (i * NW + wave) * 64 + lane;
+            const int r = L >> 4, c = (L & 15) ^ ((r & 3) << 2);
+            vdo[i] = (unsigned)(((int64_t)r * p.vs1 + c * CH) * ES);
+        }
+    }
+    auto stage_vd = [&](int kt, int buf) __attribute__((always_inline)) {
+        if constexpr (VD) {
+            const u32x4 rv = kv_rsrc_words(gv, p.vs0, p.vs1, kt * N, ES, D * ES);
+#pragma unroll
+            for (int i = 0; i < NVDI; ++i) dma16_untracked(rv, vdo[i], &sV[buf * VSZ + (i * NW + wave) * 64 * CH]);
+        }
+    };
+
     auto stage_k = [&](int kt, int buf) {
         const rsrc_t rk = kv_rsrc(gk, p.ks0, p.ks1, kt * N, ES, D * ES);
+        const u32x4 rkw = kv_rsrc_words(gk, p.ks0, p.ks1, kt * N, ES, D * ES);
 #pragma unroll
         for (int i = 0; i < NKI; ++i) {
             const int wc = (i * NW + wave) * 64;
-            if (i < NKI - 1 || wc + lane < KCH) dma16(rk, kvo[i], &sK[buf][wc * CH]);
+            if (i < NKI - 1 || wc + lane < KCH) {
+                if constexpr (VD)
+                    dma16_untracked(rkw, kvo[i], &sK[buf][wc * CH]);
+                else
+                    dma16(rk, kvo[i], &sK[buf][wc * CH]);
+            }
         }
     };
 
@@ -843,9 +874,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 #pragma unroll
                     for (int dt = 0; dt < 4; ++dt) {
                         bf16x8 a;
-                        if constexpr (F8) {
+                        if constexpr (F8 || VD) {
                             typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-                            const T *base = &sV[(FQ2 ? buf * VSZ : 0) + vt_off(dt) + (32 * u + 8 * h2) * D];
+                            const T *base = &sV[((FQ2 || VD) ? buf * VSZ : 0) + vt_off(dt) + (32 * u + 8 * h2) * D];
                             const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                                 (__attribute__((address_space(3))) bf16x4_t *)base);
                             const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -1088,15 +1119,45 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
             if (it + 1 < n_it) body(it + 1, A, B);
         }
     }
-    if (!F8 && n_it > 0) {
+    if constexpr (VD) {
+        if (n_it > 0) {
+            stage_k(kt, 0);
+            stage_vd(kt, 0);
+            if (banded(kt)) stage_slab(kt, 0);
+            wait_vmem();
+        }
+        __syncthreads();
+        for (int it = 0; it < n_it; ++it) {
+            fair_prio(it);
+            const int cur = it & 1;
+            const bool nxt = it + 1 < n_it;
+            const int kn = nxt ? next_tile() : kt;
+            const bool sahead = nxt && r_dma && banded(kn) && !banded(kt);
+            if (nxt) {
+                stage_k(kn, cur ^ 1);       // both buffers last read by the previous tile's compute
+                stage_vd(kn, cur ^ 1);
+            }
+            if (sahead) stage_slab_ahead(kn, 0);
+            if (wave_active) compute_tile(kt, cur, 0);
+            wait_vmem();
+            __syncthreads();            // tile kt consumed; kn's K, V and bias landed
+            if (nxt && banded(kn) && !sahead) {
+                stage_slab(kn, 0);
+                wait_vmem();
+                __syncthreads();
+            }
+            kt = kn;
+        }
+    }
+    if (!VD && !F8 && n_it > 0) {
         stage_k(kt, 0);
         load_v(kt);
         if (banded(kt)) stage_slab(kt, 0);
         store_v();
         wait_vmem();
     }
-    if (!F8) __syncthreads();
-    for (int it = 0; it < (F8 ? 0 : n_it); ++it) {
+    if (!VD && !F8) __syncthreads();
+    for (int it = 0; it < ((F8 || VD) ? 0 : n_it); ++it) {
         fair_prio(it);
         const int cur = it & 1;
         const bool nxt = it + 1 < n_it;
@@ -1932,6 +1993,9 @@ hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stre
     hipLaunchKernelGGL((attn_fwd_kernel<T, NW, SLAB2, PG, F8>), grid, dim3(64 * NW), 0, stream, p)
 #define RBA_FWDQ(NW, SLAB2, PG)                                                                         \
     hipLaunchKernelGGL((attn_fwd_kernel<__bf16, NW, SLAB2, PG, true, true>), grid, dim3(64 * NW), 0, stream, p)
+#define RBA_FWDV(PG)                                                                                    \
+    hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 4, false, PG, false, false, true>), grid, dim3(256), 0, stream, p)
+    const bool vd = p.G * p.QB <= 96;
     const bool fq = f8 && p.qk8;
     switch (v) {
         case AttnVariant::BF16_WIDE:    // 8 waves, 256 columns
@@ -1959,8 +2023,12 @@ hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stre
                 RBA_FWD(__bf16, 4, false, true, true);
             else if (f8)
                 RBA_FWD(__bf16, 4, false, false, true);
+            else if (paged && vd)
+                RBA_FWDV(true);
             else if (paged)
                 RBA_FWD(__bf16, 4, false, true, false);
+            else if (vd)
+                RBA_FWDV(false);
             else
                 RBA_FWD(__bf16, 4, false, false, false);
             break;
@@ -1974,6 +2042,7 @@ hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stre
     }
 #undef RBA_FWD
 #undef RBA_FWDQ
+#undef RBA_FWDV
     return hipGetLastError();
 }
 
