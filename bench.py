@@ -46,8 +46,15 @@ def log(*a):
 # (factors from a plain 1 GiB device copy under the same counters), keyed by leg and by the sha256
 # prefix of the kernel source the counters were taken on; any other source reports null.
 PROFILED_TRAFFIC = {
-    ("c3", "dae4d5990f40104b"): 6534720 * 1024 * 2 + 1049088 * 1024,
-    ("c2", "dae4d5990f40104b"): 509203 * 1024 * 2 + 131596 * 1024,
+    ("c3", "97c47d8ccc838ee3"): 6551642 * 1024 * 2 + 1049088 * 1024,
+    ("c2", "97c47d8ccc838ee3"): 505529 * 1024 * 2 + 131586 * 1024,
+    ("c4w/head-major", "97c47d8ccc838ee3"): 578560 * 1024 * 2 + 9216 * 1024,
+    ("c4f/head-major", "97c47d8ccc838ee3"): 1225728 * 1024 * 2 + 9216 * 1024,
+    ("c5/head-major", "97c47d8ccc838ee3"): 524488 * 1024 * 2 + 2064 * 1024,
+    ("c4f_mxfp8/head-major", "97c47d8ccc838ee3"): 654795 * 1024 * 2 + 12800 * 1024,
+    ("c4f_mxfp8_logits/head-major", "97c47d8ccc838ee3"): 654447 * 1024 * 2 + 9216 * 1024,
+    ("c5_mxfp8/head-major", "97c47d8ccc838ee3"): 270610 * 1024 * 2 + 5648 * 1024,
+    ("c5_mxfp8_logits/head-major", "97c47d8ccc838ee3"): 270642 * 1024 * 2 + 2064 * 1024,
 }
 
 
@@ -609,10 +616,11 @@ def main():
         extra["c4_decode_full_paged64"] = paged_decode_leg(rba, torch, "c4_decode_full", 64, 20, 8192)
         extra["c4_decode_full_paged64"]["cpu_baseline_ref"] = "workloads.c4_decode_full (same oracle and shapes)"
     if "mxfp8" in legs:
-        for name in ("c4_decode_full", "c5_long_decode"):
-            extra[name + "_mxfp8"] = decode_leg(rba, torch, name, 20, mxfp8=True)
+        for name, leg in (("c4_decode_full", "c4f"), ("c5_long_decode", "c5")):
+            extra[name + "_mxfp8"] = decode_leg(rba, torch, name, 20, mxfp8=True, leg=leg + "_mxfp8")
             extra[name + "_mxfp8"]["cpu_baseline_ref"] = f"workloads.{name} (the oracle runs on the decoded cache)"
-            extra[name + "_mxfp8_logits"] = decode_leg(rba, torch, name, 20, mxfp8=True, qk_fp8=True)
+            extra[name + "_mxfp8_logits"] = decode_leg(rba, torch, name, 20, mxfp8=True, qk_fp8=True,
+                                                       leg=leg + "_mxfp8_logits")
             extra[name + "_mxfp8_logits"]["cpu_baseline_ref"] = (f"workloads.{name} (the oracle runs on the "
                                                                  "decoded cache and the encoded q)")
     if extra:
