@@ -192,16 +192,18 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16(unsigned w, float sc) {
 // cache's rule (blocks of 32 along d), K stays as codes and scales in LDS,
 // and S^T = K . Q^T runs on v_mfma_scale_f32_32x32x64_f8f6f4, which applies
 // the E8M0 scales of both operands itself; V is decoded for PV as with F8.
-// VD (bf16, 4 waves, at most 96 query columns): V goes global -> LDS by
-// direct-to-LDS loads like K, row-major and double-buffered, and is read
-// transposed; no register staging, one barrier per tile.
+// VD (4 waves, at most 96 query columns): K and V in two buffers each beside
+// a 96-row bias slab, one barrier per tile.  bf16: V goes global -> LDS by
+// direct-to-LDS loads like K, row-major, and is read transposed.  MXFP8
+// cache (bf16 logits): the last wave, which has no columns, loads and decodes
+// the next tile's K and V while the others compute.
 template <typename T, int NW, bool SLAB2, bool PG, bool F8, bool FQ = false, bool VD = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnParams p) {
     using TL = Tile<T>;
     constexpr bool BF = sizeof(T) == 2;
     static_assert(!F8 || BF, "MXFP8 K/V is decoded to bf16");
     static_assert(!FQ || F8, "MXFP8 logits need an MXFP8 cache");
-    static_assert(!VD || (BF && !F8 && NW == 4 && !SLAB2), "VD is the 4-wave bf16 decode");
+    static_assert(!VD || (BF && !FQ && NW == 4 && !SLAB2), "VD is the 4-wave decode of bf16 or MXFP8 K/V");
     constexpr int ES = (int)sizeof(T);
     constexpr int KES = F8 ? 1 : ES;             // bytes per K/V element in memory
     constexpr int NTH = 64 * NW;                 // threads per workgroup
@@ -233,11 +235,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     // F8 otherwise: one K and one V buffer (registers carry the tiles in
     // flight).  V is row-major with 16-byte chunks XOR-swizzled by row and
     // read transposed.
-    constexpr int NKB = F8 ? (FQ2 ? 2 : 1) : 2;
+    constexpr int NKB = F8 ? ((FQ2 || VD) ? 2 : 1) : 2;
     constexpr int KBE = FQ2 ? (K8S + 4 * N) / (int)sizeof(T) : N * KS;   // elements of one K buffer
     constexpr int NVB = (FQ2 || VD) ? 2 : 1;
     constexpr int VSZ = (F8 || VD) ? N * D : TL::VROWS * VS;
-    constexpr int NSB = FQ2 ? 1 : ((SLAB2 || F8) ? 2 : 1);
+    constexpr int NSB = (FQ2 || VD) ? 1 : ((SLAB2 || F8) ? 2 : 1);
     __shared__ __attribute__((aligned(16))) T sK[NKB][KBE];
     __shared__ __attribute__((aligned(16))) T sV[NVB * VSZ];
     __shared__ __attribute__((aligned(16))) T sR[NSB][SROWS * SW];
@@ -569,32 +571,47 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     // scales of a tile through its registers (8 pieces a lane: piece i of
     // lane l is row 8 i + l / 8, 16-code piece l % 8) and decodes them, while
     // the other waves compute.
+    // (MXFP8 cache with bf16 logits, VD: K codes too, decoded into the bf16
+    // K layout.)
+    constexpr bool PK = F8 && VD;
     struct F8SetP {
-        u32x4 v[8];
+        u32x4 v[8], k[PK ? 8 : 1];
         unsigned char ks[8], vs[8];
     };
     const int pc8 = lane & 7, pr8 = lane >> 3;
+    const unsigned k8oP = (unsigned)((int64_t)pr8 * p.ks1 + 16 * pc8);
     const unsigned k8sP = (unsigned)((int64_t)pr8 * p.kss1 + (pc8 >> 1));
     const unsigned v8oP = (unsigned)((int64_t)pr8 * p.vs1 + 16 * pc8);
     const unsigned v8sP = (unsigned)((int64_t)pr8 * p.vss1 + (pc8 >> 1));
     auto load8P = [&](int kt, F8SetP &X) __attribute__((always_inline)) {
+        const rsrc_t rk = kv_rsrc(gk, p.ks0, p.ks1, kt * N, 1, D);
         const rsrc_t rks = kv_rsrc(gks, p.kss0, p.kss1, kt * N, 1, D / 32);
         const rsrc_t rv = kv_rsrc(gv, p.vs0, p.vs1, kt * N, 1, D);
         const rsrc_t rvs = kv_rsrc(gvs, p.vss0, p.vss1, kt * N, 1, D / 32);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const unsigned r = (unsigned)(8 * i);
+            if constexpr (PK) X.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k8oP + r * (unsigned)p.ks1, 0, 0);
             X.ks[i] = __builtin_amdgcn_raw_buffer_load_b8(rks, k8sP + r * (unsigned)p.kss1, 0, 0);
             X.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v8oP + r * (unsigned)p.vs1, 0, 0);
             X.vs[i] = __builtin_amdgcn_raw_buffer_load_b8(rvs, v8sP + r * (unsigned)p.vss1, 0, 0);
         }
     };
-    constexpr int kLoad8POps = 24;   // vector-memory instructions one load8P issues
+    constexpr int kLoad8POps = PK ? 32 : 24;   // vector-memory instructions one load8P issues
     auto store8P = [&](const F8SetP &X, int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int row = 8 * i + pr8;
-            if ((pc8 & 1) == 0) sK8[buf * KBB + K8S + 4 * row + (pc8 >> 1)] = X.ks[i];
+            if constexpr (PK) {
+                const float sk = e8m0_scale(X.ks[i]);
+                const u32x2 a = e4m3x4_to_bf16(X.k[i][0], sk), b2 = e4m3x4_to_bf16(X.k[i][1], sk);
+                const u32x2 c = e4m3x4_to_bf16(X.k[i][2], sk), d = e4m3x4_to_bf16(X.k[i][3], sk);
+                T *dst = &sK[buf][lds_key_row(row) * KS + 16 * pc8];
+                *(u32x4 *)dst = u32x4{a[0], a[1], b2[0], b2[1]};
+                *(u32x4 *)(dst + 8) = u32x4{c[0], c[1], d[0], d[1]};
+            } else if ((pc8 & 1) == 0) {
+                sK8[buf * KBB + K8S + 4 * row + (pc8 >> 1)] = X.ks[i];
+            }
             const float sv = e8m0_scale(X.vs[i]);
             const u32x2 a = e4m3x4_to_bf16(X.v[i][0], sv), b2 = e4m3x4_to_bf16(X.v[i][1], sv);
             const u32x2 c = e4m3x4_to_bf16(X.v[i][2], sv), d = e4m3x4_to_bf16(X.v[i][3], sv);
@@ -608,8 +625,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     // (L % 16) ^ 4 (r % 4) of key row r = L / 16, the layout the transposed
     // reads of PV expect.
     constexpr int NVDI = N * D * ES / 16 / NTH;
-    unsigned vdo[VD ? NVDI : 1] = {};
-    if constexpr (VD) {
+    unsigned vdo[(VD && !F8) ? NVDI : 1] = {};
+    if constexpr (VD && !F8) {
 #pragma unroll
         for (int i = 0; i < NVDI; ++i) {
             const int L = (i * NW + wave) * 64 + lane;
@@ -618,7 +635,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         }
     }
     auto stage_vd = [&](int kt, int buf) __attribute__((always_inline)) {
-        if constexpr (VD) {
+        if constexpr (VD && !F8) {
             const u32x4 rv = kv_rsrc_words(gv, p.vs0, p.vs1, kt * N, ES, D * ES);
 #pragma unroll
             for (int i = 0; i < NVDI; ++i) dma16_untracked(rv, vdo[i], &sV[buf * VSZ + (i * NW + wave) * 64 * CH]);
@@ -964,7 +981,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         }
     };
     int kt = n_it > 0 ? next_tile() : 0;
-    if constexpr (FQ2) {
+    // exactly one of the tile loops below runs for a configuration
+    static_assert((int)(FQ2 || PK) + (int)(F8 && !FQ2 && !PK) + (int)(VD && !F8) + (int)(!VD && !F8) == 1,
+                  "one tile loop per kernel configuration");
+    if constexpr (FQ2 || PK) {
+        // (PK: the MXFP8 cache with bf16 logits; its K codes travel with V
+        // through the staging wave, which decodes both, and the launch picks
+        // this variant only when the last wave has no columns.)
         // K codes by DMA one tile ahead into alternating buffers; V codes and
         // the scales of both two tiles ahead through registers.  The next
         // tile's V is decoded into the other buffers while this tile is
@@ -993,7 +1016,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
             const bool nxt = it + 1 < n_it, nxt2 = it + 2 < n_it;
             const int kn2 = nxt2 ? next_tile() : kn;
             sahead = nxt && r_dma && banded(kn) && !banded(kt);
-            if (nxt) stage_k8(kn, (it & 1) ^ 1);        // last read by the previous tile's compute
+            if constexpr (FQ2) {
+                if (nxt) stage_k8(kn, (it & 1) ^ 1);    // last read by the previous tile's compute
+            }
             if (sahead) stage_slab_ahead(kn, 0);
             return kn2;
         };
@@ -1001,7 +1026,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
             if (producer) {
                 F8SetP A, B;
                 if (n_it > 0) {
-                    stage_k8(kt, 0);
+                    if constexpr (FQ2) stage_k8(kt, 0);
                     load8P(kt, A);
                     load8P(kn, B);
                     if (banded(kt)) stage_slab(kt, 0);
@@ -1024,9 +1049,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
                     if (it + 1 < n_it) body(it + 1, A, B);
                 }
                 wait_vmem();
+                // no columns: nothing to write.  Leaving here makes q and O dead
+                // on this path, which the K decode's registers need.
+                if constexpr (PK) return;
             } else {
                 if (n_it > 0) {
-                    stage_k8(kt, 0);
+                    if constexpr (FQ2) stage_k8(kt, 0);
                     if (banded(kt)) stage_slab(kt, 0);
                     wait_vmem();
                 }
@@ -1039,7 +1067,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
                     tile_end(it, sahead, kn2);
                 }
             }
-        } else {
+        } else if constexpr (FQ2) {
             F8Set A, B;
             if (n_it > 0) {
                 stage_k8(kt, 0);
@@ -1070,7 +1098,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
             wait_vmem();
         }
     }
-    if constexpr (F8 && !FQ2) {
+    if constexpr (F8 && !FQ2 && !PK) {
         // Two tiles in flight: while tile kt is computed from LDS, the codes of
         // tile kn wait in one register set and those of the tile after it load
         // into the other; each iteration decodes kn into the (single) K and V
@@ -1119,7 +1147,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
             if (it + 1 < n_it) body(it + 1, A, B);
         }
     }
-    if constexpr (VD) {
+    if constexpr (VD && !F8) {
         if (n_it > 0) {
             stage_k(kt, 0);
             stage_vd(kt, 0);
@@ -2019,6 +2047,12 @@ hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stre
                 RBA_FWDQ(4, false, true);
             else if (fq)
                 RBA_FWDQ(4, false, false);
+            else if (f8 && paged && vd)
+                hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 4, false, true, true, false, true>), grid, dim3(256), 0,
+                                   stream, p);
+            else if (f8 && vd)
+                hipLaunchKernelGGL((attn_fwd_kernel<__bf16, 4, false, false, true, false, true>), grid, dim3(256), 0,
+                                   stream, p);
             else if (f8 && paged)
                 RBA_FWD(__bf16, 4, false, true, true);
             else if (f8)
