@@ -131,6 +131,13 @@ F8_CASES = [
     ("decode_swa_log", dict(B=2, Sq=5, Skv=777, Hq=16, Hkv=2, E=96, window=300, log_scale_base=64.0), [1, 4]),
     ("long_sq1", dict(B=1, Sq=1, Skv=3000, Hq=8, Hkv=1, E=64, window=0, log_scale_base=4096.0), [1, 8]),
     ("wide_prefill", dict(B=1, Sq=300, Skv=300, Hq=16, Hkv=2, E=64, window=96), [1]),
+    # every key tile carries bias: consecutive banded tiles share the one bias buffer of the
+    # staging-wave kernels, which then reload it between two barriers
+    ("all_banded", dict(B=2, Sq=9, Skv=400, Hq=16, Hkv=2, E=512, window=0), [1, 3]),
+    # bias rows not 16-byte aligned: the bias windows go through registers
+    ("unaligned_E", dict(B=2, Sq=9, Skv=500, Hq=16, Hkv=2, E=100, window=0), [1]),
+    # 112 query columns: no wave without columns, every thread decodes its share
+    ("wide_g112", dict(B=2, Sq=1, Skv=600, Hq=112, Hkv=1, E=64, window=0), [1, 2]),
 ]
 
 

@@ -481,6 +481,21 @@ def test_one_hot_bias_exact_unaligned_rows(dstar, window):
     one_hot_case(1, 333, 333, 100, 16, 2, dstar, window, False)
 
 
+@pytest.mark.parametrize("dstar,window", [(0, 0), (1, 0), (99, 0), (37, 60)])
+def test_one_hot_bias_exact_decode_unaligned_rows(dstar, window):
+    """Decode (72 query columns, the kernel that loads V by DMA) with an
+    extent of 100: bias rows not 16-byte aligned, staged by element loads."""
+    one_hot_case(1, 333, 9, 100, 16, 2, dstar, window, True)
+
+
+@pytest.mark.parametrize("dstar,window", [(0, 0), (1, 0), (300, 0), (390, 0), (5, 200)])
+def test_one_hot_bias_exact_decode_all_banded(dstar, window):
+    """Decode with every key tile inside the extent (E = 512 over 400 keys):
+    consecutive banded tiles share the single bias buffer, which is then
+    reloaded between two barriers."""
+    one_hot_case(2, 400, 9, 512, 16, 2, dstar, window, True)
+
+
 @pytest.mark.parametrize("dstar,window", [(0, 0), (1, 0), (511, 0), (300, 700), (64, 0)])
 def test_one_hot_bias_exact_persistent_rounds(dstar, window):
     """The prefill workloads' heads and extent (Hq = 64, Hkv = 8, E = 512) at
