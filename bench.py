@@ -276,7 +276,9 @@ def decode_leg(rba, torch, name, reps, mxfp8=False, leg=None, cpu_budget=0.0, qk
     ms_warm = time_launches(launch, reps, torch)
     ms = time_cold(launch, max(reps, 50), torch)
     gbs = kv_bytes / (ms * 1e-3) / 1e9
-    kname = ("attn_fwd_kernel<bf16, 4 waves" + (", MXFP8" if mxfp8 else "") + (" logits" if qk_fp8 else "") + ">"
+    # the 4-wave variant the library picks for at most 96 query columns (72 and 8 here)
+    kname = ("attn_fwd_kernel<bf16, 4 waves, "
+             + ("MXFP8 logits, staging wave" if qk_fp8 else ("MXFP8 cache, staging wave" if mxfp8 else "V by DMA")) + ">"
              + (" + combine_kernel" if splits > 1 else ""))
     res = {"ms": round(ms, 4), "kv_GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
            "ms_warm": round(ms_warm, 4), "num_splits": splits, "kv_bytes": kv_bytes,
@@ -340,6 +342,11 @@ def paged_decode_leg(rba, torch, name, page_size, reps, len_lo, seed=77):
         kv_bytes += (L - lo) * w.Hkv * w.d * 2 * 2
     gbs = kv_bytes / (ms * 1e-3) / 1e9
     res = {"ms": round(ms, 4), "kv_GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic("c4f_paged64/head-major"),
+                        "kernel": "attn_fwd_kernel<bf16, 4 waves, paged, V by DMA>" + (" + combine_kernel" if splits > 1
+                                                                                      else ""),
+                        "avg_ms": round(ms, 4), "algorithmic_bytes": kv_bytes},
            "ms_warm": round(ms_warm, 4), "num_splits": splits, "kv_bytes": kv_bytes, "page_size": page_size,
            "seq_lens": f"uniform in [{len_lo}, {w.Skv}], seed {seed}",
            "cache": "pages stored head-major [Hkv, page_size, d], passed as strided [page_size, Hkv, d] views",
