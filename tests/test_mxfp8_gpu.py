@@ -138,6 +138,8 @@ F8_CASES = [
     ("unaligned_E", dict(B=2, Sq=9, Skv=500, Hq=16, Hkv=2, E=100, window=0), [1]),
     # 112 query columns: no wave without columns, every thread decodes its share
     ("wide_g112", dict(B=2, Sq=1, Skv=600, Hq=112, Hkv=1, E=64, window=0), [1, 2]),
+    # exactly 96 query columns: three full waves and the staging wave
+    ("cols96", dict(B=2, Sq=6, Skv=500, Hq=32, Hkv=2, E=64, window=0), [1, 2]),
 ]
 
 

@@ -418,6 +418,20 @@ def test_decode_small_head_major_cache(name, over, splits):
     assert torch.equal(o, o_tm) and torch.equal(lse, lse_tm)
 
 
+@pytest.mark.parametrize("Sq", [6, 7])
+def test_decode_column_boundary(Sq):
+    """16 query heads a kv head: 96 columns (the 4-wave kernel with V by DMA and
+    a 96-row bias slab) and 112 (the general 4-wave kernel), dense and paged."""
+    w = small(CONFIGS["c4_decode_full"], B=2, Sq=Sq, Skv=600, Hq=32, Hkv=2, E=64, window=0)
+    say(f"decode columns {16 * Sq}: {w}")
+    inp = make_inputs(w)
+    wo, wl = oracle_full(inp, w)
+    for splits in (1, 3):
+        o, lse = run_path(inp, w, decode=True, splits=splits)
+        check(f"columns {16 * Sq}/{splits} o", o, wo, False)
+        check(f"columns {16 * Sq}/{splits} lse", lse, wl, True, extra_tol=2e-2)
+
+
 def test_decode_split_invariance_and_prefill_agreement():
     m = rba()
     w = small(CONFIGS["c4_decode_full"], B=2, Sq=9, Skv=1200, Hq=16, Hkv=2, E=64, window=0)
