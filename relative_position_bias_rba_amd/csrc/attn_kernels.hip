@@ -583,7 +583,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
     const unsigned k8sP = (unsigned)((int64_t)pr8 * p.kss1 + (pc8 >> 1));
     const unsigned v8oP = (unsigned)((int64_t)pr8 * p.vs1 + 16 * pc8);
     const unsigned v8sP = (unsigned)((int64_t)pr8 * p.vss1 + (pc8 >> 1));
-    auto load8P = [&](int kt, F8SetP &X) __attribute__((always_inline)) {
+    auto load8P = [&](int kt, F8SetP &X, auto role_c) __attribute__((always_inline)) {
+        constexpr int ROLE = decltype(role_c)::value;     // 0: K and V, 1: K only, 2: V only
         const rsrc_t rk = kv_rsrc(gk, p.ks0, p.ks1, kt * N, 1, D);
         const rsrc_t rks = kv_rsrc(gks, p.kss0, p.kss1, kt * N, 1, D / 32);
         const rsrc_t rv = kv_rsrc(gv, p.vs0, p.vs1, kt * N, 1, D);
@@ -591,18 +592,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const unsigned r = (unsigned)(8 * i);
-            if constexpr (PK) X.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k8oP + r * (unsigned)p.ks1, 0, 0);
-            X.ks[i] = __builtin_amdgcn_raw_buffer_load_b8(rks, k8sP + r * (unsigned)p.kss1, 0, 0);
-            X.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v8oP + r * (unsigned)p.vs1, 0, 0);
-            X.vs[i] = __builtin_amdgcn_raw_buffer_load_b8(rvs, v8sP + r * (unsigned)p.vss1, 0, 0);
+            if constexpr (ROLE != 2) {
+                if constexpr (PK) X.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k8oP + r * (unsigned)p.ks1, 0, 0);
+                X.ks[i] = __builtin_amdgcn_raw_buffer_load_b8(rks, k8sP + r * (unsigned)p.kss1, 0, 0);
+            }
+            if constexpr (ROLE != 1) {
+                X.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v8oP + r * (unsigned)p.vs1, 0, 0);
+                X.vs[i] = __builtin_amdgcn_raw_buffer_load_b8(rvs, v8sP + r * (unsigned)p.vss1, 0, 0);
+            }
         }
     };
-    constexpr int kLoad8POps = PK ? 32 : 24;   // vector-memory instructions one load8P issues
-    auto store8P = [&](const F8SetP &X, int buf) __attribute__((always_inline)) {
+    // vector-memory instructions one load8P of a role issues
+    auto load8P_ops = [](int role) constexpr { return role == 0 ? (PK ? 32 : 24) : (role == 1 ? (PK ? 16 : 8) : 16); };
+    auto store8P = [&](const F8SetP &X, int buf, auto role_c) __attribute__((always_inline)) {
+        constexpr int ROLE = decltype(role_c)::value;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int row = 8 * i + pr8;
-            if constexpr (PK) {
+            if constexpr (ROLE == 2) {
+            } else if constexpr (PK) {
                 const float sk = e8m0_scale(X.ks[i]);
                 const u32x2 a = e4m3x4_to_bf16(X.k[i][0], sk), b2 = e4m3x4_to_bf16(X.k[i][1], sk);
                 const u32x2 c = e4m3x4_to_bf16(X.k[i][2], sk), d = e4m3x4_to_bf16(X.k[i][3], sk);
@@ -612,6 +620,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
             } else if ((pc8 & 1) == 0) {
                 sK8[buf * KBB + K8S + 4 * row + (pc8 >> 1)] = X.ks[i];
             }
+            if constexpr (ROLE == 1) continue;
             const float sv = e8m0_scale(X.vs[i]);
             const u32x2 a = e4m3x4_to_bf16(X.v[i][0], sv), b2 = e4m3x4_to_bf16(X.v[i][1], sv);
             const u32x2 c = e4m3x4_to_bf16(X.v[i][2], sv), d = e4m3x4_to_bf16(X.v[i][3], sv);
@@ -997,7 +1006,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         // The single bias buffer is loaded ahead when the tile being computed
         // carries no bias, else after the barrier (then a second one).
         const bool split = (NW - 1) * 32 >= ncols;          // the last wave has no columns
-        const bool producer = split && wave == NW - 1;
+        // MXFP8 cache with two waves without columns: the last decodes V, the
+        // one before it K; otherwise the last wave decodes both
+        const bool split2 = PK && (NW - 2) * 32 >= ncols;
+        const bool producer = split && (wave == NW - 1 || (split2 && wave == NW - 2));
         int kn = n_it > 1 ? next_tile() : kt;
         // the barriers of one tile, common to both roles; returns kn's successor
         auto tile_end = [&](int it, bool sahead, int kn2) __attribute__((always_inline)) {
@@ -1024,31 +1036,41 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
         };
         if (split) {
             if (producer) {
-                F8SetP A, B;
-                if (n_it > 0) {
-                    if constexpr (FQ2) stage_k8(kt, 0);
-                    load8P(kt, A);
-                    load8P(kn, B);
-                    if (banded(kt)) stage_slab(kt, 0);
-                    store8P(A, 0);
+                auto stage = [&](auto role_c) __attribute__((always_inline)) {
+                    constexpr int ROLE = decltype(role_c)::value;
+                    constexpr int OPS = load8P_ops(ROLE);
+                    F8SetP A, B;
+                    if (n_it > 0) {
+                        if constexpr (FQ2) stage_k8(kt, 0);
+                        load8P(kt, A, role_c);
+                        load8P(kn, B, role_c);
+                        if (banded(kt)) stage_slab(kt, 0);
+                        store8P(A, 0, role_c);
+                        wait_vmem();
+                    }
+                    __syncthreads();
+                    auto body = [&](int it, F8SetP &X, F8SetP &Y) __attribute__((always_inline)) {
+                        bool sahead;
+                        const int kn2 = tile_begin(it, sahead);
+                        // issued on every tile (the last two repeat a tile and are
+                        // never stored), so that every path carries the same count
+                        load8P(kn2, Y, role_c);
+                        if (it + 1 < n_it) store8P(X, (it & 1) ^ 1, role_c);
+                        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS) : "memory");
+                        tile_end(it, sahead, kn2);
+                    };
+                    for (int it = 0; it < n_it; it += 2) {
+                        body(it, B, A);
+                        if (it + 1 < n_it) body(it + 1, A, B);
+                    }
                     wait_vmem();
-                }
-                __syncthreads();
-                auto body = [&](int it, F8SetP &X, F8SetP &Y) __attribute__((always_inline)) {
-                    bool sahead;
-                    const int kn2 = tile_begin(it, sahead);
-                    // issued on every tile (the last two repeat a tile and are
-                    // never stored), so that every path carries the same count
-                    load8P(kn2, Y);
-                    if (it + 1 < n_it) store8P(X, (it & 1) ^ 1);
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoad8POps) : "memory");
-                    tile_end(it, sahead, kn2);
                 };
-                for (int it = 0; it < n_it; it += 2) {
-                    body(it, B, A);
-                    if (it + 1 < n_it) body(it + 1, A, B);
-                }
-                wait_vmem();
+                if (!split2)
+                    stage(std::integral_constant<int, 0>{});
+                else if (wave == NW - 1)
+                    stage(std::integral_constant<int, 2>{});
+                else
+                    stage(std::integral_constant<int, 1>{});
                 // no columns: nothing to write.  Leaving here makes q and O dead
                 // on this path, which the K decode's registers need.
                 if constexpr (PK) return;
