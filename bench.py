@@ -46,15 +46,16 @@ def log(*a):
 # (factors from a plain 1 GiB device copy under the same counters), keyed by leg and by the sha256
 # prefix of the kernel source the counters were taken on; any other source reports null.
 PROFILED_TRAFFIC = {
-    ("c3", "97c47d8ccc838ee3"): 6551642 * 1024 * 2 + 1049088 * 1024,
-    ("c2", "97c47d8ccc838ee3"): 505529 * 1024 * 2 + 131586 * 1024,
-    ("c4w/head-major", "97c47d8ccc838ee3"): 578560 * 1024 * 2 + 9216 * 1024,
-    ("c4f/head-major", "97c47d8ccc838ee3"): 1225728 * 1024 * 2 + 9216 * 1024,
-    ("c5/head-major", "97c47d8ccc838ee3"): 524488 * 1024 * 2 + 2064 * 1024,
-    ("c4f_mxfp8/head-major", "97c47d8ccc838ee3"): 654795 * 1024 * 2 + 12800 * 1024,
-    ("c4f_mxfp8_logits/head-major", "97c47d8ccc838ee3"): 654447 * 1024 * 2 + 9216 * 1024,
-    ("c5_mxfp8/head-major", "97c47d8ccc838ee3"): 270610 * 1024 * 2 + 5648 * 1024,
-    ("c5_mxfp8_logits/head-major", "97c47d8ccc838ee3"): 270642 * 1024 * 2 + 2064 * 1024,
+    ("c3", "4bb384e9d4699580"): 6543443 * 1024 * 2 + 1049088 * 1024,
+    ("c2", "4bb384e9d4699580"): 508752 * 1024 * 2 + 131594 * 1024,
+    ("c4w/head-major", "4bb384e9d4699580"): 578560 * 1024 * 2 + 9216 * 1024,
+    ("c4f/head-major", "4bb384e9d4699580"): 1225728 * 1024 * 2 + 9216 * 1024,
+    ("c5/head-major", "4bb384e9d4699580"): 524484 * 1024 * 2 + 2064 * 1024,
+    ("c4f_paged64/head-major", "4bb384e9d4699580"): 1163403 * 1024 * 2 + 9218 * 1024,
+    ("c4f_mxfp8/head-major", "4bb384e9d4699580"): 654424 * 1024 * 2 + 9216 * 1024,
+    ("c4f_mxfp8_logits/head-major", "4bb384e9d4699580"): 654448 * 1024 * 2 + 9216 * 1024,
+    ("c5_mxfp8/head-major", "4bb384e9d4699580"): 270643 * 1024 * 2 + 2064 * 1024,
+    ("c5_mxfp8_logits/head-major", "4bb384e9d4699580"): 270647 * 1024 * 2 + 2064 * 1024,
 }
 
 
