@@ -176,17 +176,23 @@ size_t rba_prefill_fused_workspace_bytes(const rba_attn_args *args);
 
 /* rba_relproj and rba_attn_prefill in one launch ([S-RPB]): the same outputs,
  * bit for bit, as rba_relproj (bf16 out) into an R that rba_attn_prefill then
- * reads, but each workgroup computes the rows of R its query block needs
- * (all E distances of its rows, on MFMA) into its region of `workspace` and
- * reads them from there, so R never makes the round trip through HBM.
+ * reads, with the relative logits computed inside the attention kernel on
+ * MFMA, in one of two ways:
+ *   workspace given: each workgroup computes the rows of R its query block
+ *     needs (all E distances of its rows) into its region of `workspace` and
+ *     reads them from there, so no R for the whole problem is materialised;
+ *   workspace NULL (r_dim <= 64): each wave computes, for every key tile that
+ *     meets distances below E, the logits of its query columns that the tile
+ *     needs straight into LDS: no R is written to memory at all.
+ * With r_dim > 64 the workspace is required.
  * args->R must be NULL (the bias comes from rb); args->E is the extent (>= 1).
  * Supported where rba_attn_prefill runs its two-group bf16 kernel: bf16,
  * plain K/V, (Hq/Hkv) * min(Sq, 32) > 128, K/V spans of one (batch, kv
  * head) under 2^31 bytes; otherwise RBA_E_UNSUPPORTED.  Returns
- * RBA_E_WORKSPACE if workspace is NULL, unaligned (16 bytes) or smaller than
- * rba_prefill_fused_workspace_bytes(args).  The workspace is scratch: its
- * contents before and after the call carry no meaning; two calls in flight
- * at once need two workspaces.                                               */
+ * RBA_E_WORKSPACE if a workspace is given but unaligned (16 bytes) or smaller
+ * than rba_prefill_fused_workspace_bytes(args), or if it is NULL with
+ * r_dim > 64.  The workspace is scratch: its contents before and after the
+ * call carry no meaning; two calls in flight at once need two workspaces.   */
 rba_status rba_attn_prefill_fused(const rba_attn_args *args, const rba_relbias *rb, void *workspace,
                                   size_t workspace_bytes, void *stream);
 

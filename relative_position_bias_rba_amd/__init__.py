@@ -311,10 +311,12 @@ def prefill_fused_workspace_bytes(q, k, v, E: int, *, window=0) -> int:
 
 
 def attn_prefill_fused(q, k, v, r, PT: PackedProjection, *, per_head=False, window=0, scale=None,
-                       log_scale_base=0.0, return_lse=False, out=None, workspace=None):
-    """relproj + attn_prefill in one launch: each workgroup computes the rows
-    of R its query block needs from r and the packed projection PT
-    (relproj_pack) and keeps them in its region of the workspace."""
+                       log_scale_base=0.0, return_lse=False, out=None, workspace=None, on_chip=False):
+    """relproj + attn_prefill in one launch, the relative logits computed inside
+    the attention kernel from r and the packed projection PT (relproj_pack):
+    by default each workgroup keeps the rows of R of its query block in its
+    region of a workspace; on_chip=True (r_dim <= 64) computes each banded key
+    tile's logits straight into LDS, with no workspace and no R in memory."""
     _check_attn_inputs(q, k, v, None)
     if not (r.is_cuda and PT.data.is_cuda) or r.dtype != q.dtype or PT.data.dtype != q.dtype:
         raise TypeError("r and PT must be GPU tensors of q's dtype")
@@ -326,6 +328,12 @@ def attn_prefill_fused(q, k, v, r, PT: PackedProjection, *, per_head=False, wind
     a = make_args(q, k, v, None, o, lse, window=window, scale=scale, log_scale_base=log_scale_base)
     a.E = PT.E
     rb = make_relbias(r, PT, per_head)
+    if on_chip:
+        if workspace is not None:
+            raise ValueError("on_chip takes no workspace")
+        code = _lib.rba_attn_prefill_fused(ctypes.byref(a), ctypes.byref(rb), None, 0, _stream(q.device))
+        _check("rba_attn_prefill_fused", code)
+        return (o, lse) if return_lse else o
     need = _lib.rba_prefill_fused_workspace_bytes(ctypes.byref(a))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

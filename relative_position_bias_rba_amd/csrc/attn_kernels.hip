@@ -1369,9 +1369,99 @@ __device__ __forceinline__ void bias_rows(const AttnParams &p, __bf16 *ws, int b
     }
 }
 
+// Relative logits of one banded key tile for the wave's 32 query columns,
+// computed on the matrix cores straight into the wave's own slab in LDS
+// ([S-RPB]: R[t, h, e] = r_t . P_h[:, e]), so that R never goes to memory.
+// The tile's keys j0..j0+63 meet, over the block's rows, the distances lo =
+// p_min - j0 - 63 up to lo + 63 + nrows - 1; they are computed in (at most
+// four) tiles of 32 distances from the aligned one holding lo, with
+// relproj_kernel's operands in its order (A = packed P^T fragments, B = r,
+// k-steps ascending, fp32 accumulation, one rounding to bf16): the slab holds
+// rba_relproj's values bit for bit.  Column lc's entry for distance e sits at
+// slab[lc * SWD + e - 32 floor(lo / 32)]; distance tiles outside 0..E-1, and
+// columns without a query row, hold zeros.  Only this wave reads its slab,
+// and LDS operations of one wave complete in order, so no barrier is needed.
+template <int FK, int SWD>
+__device__ __forceinline__ void bias_tile(const AttnParams &p, __bf16 *slab, int b, int hkv, int t0, int nrows,
+                                          int lo, int wave, int lane_in) {
+    typedef __bf16 T;
+    // the lane's addresses are derived here on every call, not held in
+    // registers across the tile loop
+    int lane = lane_in;
+    asm volatile("" : "+v"(lane));
+    const int lc = lane & 31, hh = lane >> 5;
+    const int col = wave * 32 + lc;
+    const int hl = col / p.QB, qi = col - hl * p.QB;
+    const bool valid = col < p.G * p.QB && qi < nrows;
+    const int hq = hkv * p.G + min(hl, p.G - 1);
+    const int nks = p.r_dim >> 4;
+    const int nEB = (p.E + 31) >> 5;
+    const int eb_lo = lo >> 5;                                // floor, also for lo < 0
+    const int nb = ((lo + 63 + nrows - 1) >> 5) - eb_lo + 1;   // 2..4
+    const T *rrow = (const T *)p.rf + (int64_t)b * p.rfs0 + (int64_t)(t0 + (valid ? qi : 0)) * p.rfs1 +
+                    (int64_t)hq * p.rfs2 + 8 * hh;
+    const int h_lo = (wave * 32) / p.QB;
+    const int h_hi = min((wave * 32 + 31) / p.QB, p.G - 1);
+    const int hspan = nEB * nks * 512;   // packed entries of one head
+    T *dst = slab + lc * SWD + 16 * hh;
+    for (int hp = h_lo; hp <= h_hi; ++hp) {
+        const rsrc_t rP = make_rsrc((const T *)p.PT + (int64_t)(hkv * p.G + hp) * hspan, (int64_t)hspan * 2);
+        // a lane without a query row writes zeros (its B operand is zero) once
+        const bool mine = valid ? hl == hp : hp == h_lo;
+        // k-steps past r_dim multiply a zero B operand.  Every load is
+        // unconditional (k-step clamped to the last one, distance tile into
+        // 0..nEB-1, so all stay inside the head's operands) and each wait
+        // below covers only the loads it needs; a distance tile outside
+        // 0..nEB-1 writes zeros.
+        auto load_a = [&](bf16x8 (&a)[FK], int j) __attribute__((always_inline)) {
+            const int eb = min(max(eb_lo + j, 0), nEB - 1);
+#pragma unroll
+            for (int k = 0; k < FK; ++k)
+                a[k] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rP, (unsigned)lane * 16, (eb * nks + min(k, nks - 1)) * 1024, 0));
+        };
+        bf16x8 rfr[FK], a0[FK];
+#pragma unroll
+        for (int k = 0; k < FK; ++k) rfr[k] = *(const bf16x8 *)(rrow + 16 * min(k, nks - 1));
+        load_a(a0, 0);
+        __builtin_amdgcn_sched_barrier(0);   // all in flight before the first wait
+#pragma unroll
+        for (int k = 0; k < FK; ++k) rfr[k] = (valid && k < nks) ? rfr[k] : bf16x8{};
+        auto tile = [&](const bf16x8 (&a)[FK], int j) __attribute__((always_inline)) {
+            f32x16 acc = f32x16{};
+#pragma unroll
+            for (int k = 0; k < FK; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k], rfr[k], acc, 0, 0, 0);
+            const bool live = eb_lo + j >= 0 && eb_lo + j < nEB;
+            if (mine) {
+                bf16x8 w0, w1;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    w0[x] = live ? (__bf16)acc[x] : (__bf16)0.f;
+                    w1[x] = live ? (__bf16)acc[8 + x] : (__bf16)0.f;
+                }
+                *(bf16x8 *)(dst + 32 * j) = w0;
+                *(bf16x8 *)(dst + 32 * j + 8) = w1;
+            }
+        };
+        // one register set: each distance tile waits for its own loads
+        tile(a0, 0);
+#pragma unroll
+        for (int j = 1; j < 4; ++j) {
+            if (j >= nb) break;
+            load_a(a0, j);
+            __builtin_amdgcn_sched_barrier(0);   // the tile's four loads in flight together
+            tile(a0, j);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // FK = 0: bias rows read from R; FK > 0: computed by bias_rows<FK> into the
-// workgroup's region of bias_ws.
-template <int FK>
+// workgroup's region of bias_ws; ONC (FK = 4): each banded tile's bias
+// computed by bias_tile into the wave's slab, no R rows in memory at all.
+template <int FK, bool ONC = false>
 __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParams p_arg) {
     typedef const __attribute__((address_space(4))) AttnParams CParams;
     typedef __bf16 T;
@@ -1393,8 +1483,11 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     constexpr int NKI = (KCH + GT - 1) / GT;     // 5
     constexpr int NVI = VCH / GT;                // 4
     constexpr int NSI = (HCH + GT - 1) / GT;     // 5 per group half
-    constexpr int NSLOT = NKI + NVI + 2 * NSI;   // DMA instructions per issuing lane and phase
+    constexpr int NSLOT = ONC ? NKI + NVI : NKI + NVI + 2 * NSI;   // DMA instructions per issuing lane and phase
     static_assert(NKI == 5 && NVI * GT == VCH && NSI == 5, "staging split");
+    static_assert(!ONC || FK == 4, "the on-chip bias holds four k-steps of r");
+    constexpr int SWD = 136;                     // on-chip slab row: four distance tiles + padding
+    static_assert(!ONC || 8 * 32 * SWD <= 2 * 2 * NSI * GT * CH, "on-chip slabs fit the bias buffers");
 
     __shared__ __attribute__((aligned(16))) T sK[2][NKI * GT * CH];
     __shared__ __attribute__((aligned(16))) T sV[2][N * D];
@@ -1479,7 +1572,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     const bool wave_active = wave * 32 < ncols;
     const int rb = (prow - N + 1) & ~(CH - 1);
 
-    if constexpr (FK > 0) {
+    if constexpr (FK > 0 && !ONC) {
         if (has_bias) {
             if (wave_active)
                 bias_rows<FK>(p, (__bf16 *)p.bias_ws + (int64_t)blockIdx.x * p.G * ((p.E + 31) >> 5) * p.QB * 32,
@@ -1603,12 +1696,14 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
         } else if (s < NKI + NVI) {
             const int i = s - NKI;
             if (dv) dma16_untracked(rv, vvo[i], &sV[vbuf][(i * GT + gw * 64) * CH]);
-        } else if (s < NKI + NVI + NSI) {
-            const int i = s - NKI - NVI;
-            if (ds0) dma16_untracked(rR4, svo[0][i] + s0off, &sR[0][s0buf][(i * GT + gw * 64) * CH]);
-        } else {
-            const int i = s - NKI - NVI - NSI;
-            if (ds1) dma16_untracked(rR4, svo[1][i] + s1off, &sR[1][s1buf][(i * GT + gw * 64) * CH]);
+        } else if constexpr (!ONC) {
+            if (s < NKI + NVI + NSI) {
+                const int i = s - NKI - NVI;
+                if (ds0) dma16_untracked(rR4, svo[0][i] + s0off, &sR[0][s0buf][(i * GT + gw * 64) * CH]);
+            } else {
+                const int i = s - NKI - NVI - NSI;
+                if (ds1) dma16_untracked(rR4, svo[1][i] + s1off, &sR[1][s1buf][(i * GT + gw * 64) * CH]);
+            }
         }
     };
     // bias rows not 16-byte aligned: element loads through registers
@@ -1650,6 +1745,10 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     // ------------------------------------------------------------ phase work
     const int kr0 = lds_key_row(mfma_row_key(lc));
     const int s_lane = (col - grp * HROWS) * SW + (prow - rb) - 16 * hh;
+    // on-chip bias: the wave's slab, and the lane's entry offset in it (the
+    // same for every key tile: 32 floor((p_min - 63 - j0) / 32) + j0 is fixed)
+    T *const sB = &sR[0][0][0] + wave * 32 * SWD;
+    const int s_lane_b = lc * SWD + (prow - (((p_min - (N - 1)) >> 5) << 5)) - 16 * hh;
     // V^T fragment of PV step (u, h2, dt): two transpose reads of 4 keys each.
     // Lane (g = lane / 16, a = lane % 4, i = lane / 4 % 4) addresses key row
     // 32u + 16(g / 2) + 8h2 + 4x + i and head-dim entries 32dt + 16(g % 2) + 4a,
@@ -1716,13 +1815,18 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
                 for (int s = s0; s < s1; ++s) issue(s);
             }
         };
-        burst(0, 6);
         const int j0 = kt * N;
         const bool band = banded(kt);
+        if constexpr (ONC) {
+            if (band) bias_tile<FK, SWD>(p, sB, b, hkv, t0, nrows, p_min - j0 - (N - 1), wave, lane);
+        }
+        burst(0, 6);
         const bool edge = !((j0 + N - 1 <= p_min) && (W == 0 || p_max - j0 < W));
         float mt = -INFINITY;
         if (band || edge) {
-            const T *sr = &sR[grp][t & 1][s_lane];
+            int slb = s_lane_b;
+            if constexpr (ONC) asm volatile("" : "+v"(slb));   // one address register, offsets folded in
+            const T *sr = ONC ? sB + slb : &sR[grp][t & 1][s_lane];
             const bool partial = p_max - j0 >= p.E;
             const int elim = prow - j0 - 16 * hh - p.E;   // key offset r of a half has e < E iff r > elim
             const int dbase = prow - j0 - 16 * hh;        // distance of key offset 0 of this half
@@ -2021,6 +2125,12 @@ int fused_grid(int64_t items, int cus) {
 }
 
 hipError_t launch_attention_fused(const AttnParams &p, int grid, hipStream_t stream) {
+    if (p.bias_ws == nullptr) {   // the bias of each banded tile computed into LDS (r_dim <= 64)
+        const int64_t items = (int64_t)p.B * p.Hkv * p.nqb;
+        if (items <= 0) return hipSuccess;
+        hipLaunchKernelGGL((attn_prefill_pp_kernel<4, true>), dim3(pp_grid(items)), dim3(512), 0, stream, p);
+        return hipGetLastError();
+    }
     if (grid <= 0) return hipSuccess;
     if (p.r_dim <= 64)
         hipLaunchKernelGGL(attn_prefill_pp_kernel<4>, dim3(grid), dim3(512), 0, stream, p);

@@ -246,11 +246,15 @@ rba_status rba_attn_prefill_fused(const rba_attn_args *args, const rba_relbias *
     if (rb->r == nullptr || rb->PT == nullptr || !aligned(rb->r, 16) || !aligned(rb->PT, 16)) return RBA_E_INVALID;
     if (!strides_ok(rb->r_s, 8)) return RBA_E_INVALID;
     if (rb->r_s[2] != 0 && rb->r_s[2] < rb->r_dim) return RBA_E_INVALID;
+    // no workspace: the logits of each banded key tile are computed into LDS
+    // (features of at most 64 channels)
+    const bool on_chip = workspace == nullptr;
+    if (on_chip && rb->r_dim > 64) return RBA_E_WORKSPACE;
     const int cus = device_cus();
     if (cus <= 0) return RBA_E_LAUNCH;
     const Plan pl = make_plan(args);
     const size_t need = fused_workspace(args, pl, cus);
-    if (workspace == nullptr || workspace_bytes_ < need || !aligned(workspace, 16)) return RBA_E_WORKSPACE;
+    if (!on_chip && (workspace_bytes_ < need || !aligned(workspace, 16))) return RBA_E_WORKSPACE;
     rba::AttnParams p = make_params(args, pl, 1);
     p.E = args->E;
     p.rf = rb->r;

@@ -85,7 +85,9 @@ int attn_max_columns(AttnVariant v);
 hipError_t launch_attention(const AttnParams &p, AttnVariant v, hipStream_t stream);
 
 // The prefill kernel with the relative logits computed in place (p.rf set):
-// `grid` workgroups, each owning bias_ws rows QB*G*E of its own.
+// `grid` workgroups, each owning bias_ws rows QB*G*E of its own; with
+// bias_ws null (r_dim <= 64) each banded tile's logits are computed into LDS
+// instead and `grid` is not used.
 hipError_t launch_attention_fused(const AttnParams &p, int grid, hipStream_t stream);
 
 // Workgroups the fused prefill kernel runs with for `items` work items on a

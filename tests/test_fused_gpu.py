@@ -51,12 +51,12 @@ def per_head_r(inp, w, seed):
     return (torch.randn(w.B, w.Sq, w.Hq, w.r_dim, generator=g) * w.r_std).to(torch.bfloat16)
 
 
-def both_paths(d, w, r, per_head):
+def both_paths(d, w, r, per_head, on_chip=False):
     """(fused o, lse), (relproj + prefill o, lse) on the same device inputs."""
     m = rba()
     PT = m.relproj_pack(d["P"])
     kw = dict(window=w.window, log_scale_base=w.log_scale_base, return_lse=True)
-    of, lf = m.attn_prefill_fused(d["q"], d["k"], d["v"], r, PT, per_head=per_head, **kw)
+    of, lf = m.attn_prefill_fused(d["q"], d["k"], d["v"], r, PT, per_head=per_head, on_chip=on_chip, **kw)
     R = m.relproj(r, d["P"], per_head=per_head)
     ou, lu = m.attn_prefill(d["q"], d["k"], d["v"], R, **kw)
     torch.cuda.synchronize()
@@ -111,15 +111,18 @@ FUSED_CASES = [
 ]
 
 
+@pytest.mark.parametrize("on_chip", [False, True], ids=["workspace", "on_chip"])
 @pytest.mark.parametrize("name,over,ph", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
-def test_fused_prefill_parity(name, over, ph):
+def test_fused_prefill_parity(name, over, ph, on_chip):
     w = scaled(CONFIGS["c2_swa_prefill"], **over)
-    say(f"fused {name}: {w} per_head={ph}")
+    if on_chip and w.r_dim > 64:
+        pytest.skip("the on-chip path takes features of at most 64 channels")
+    say(f"fused {name}: {w} per_head={ph} on_chip={on_chip}")
     inp = make_inputs(w)
     if ph:
         inp["r"] = per_head_r(inp, w, 17)
     d = {k: v.to(DEV) for k, v in inp.items()}
-    (of, lf), (ou, lu) = both_paths(d, w, d["r"], ph)
+    (of, lf), (ou, lu) = both_paths(d, w, d["r"], ph, on_chip)
     assert torch.equal(of, ou), f"{name}: fused and two-kernel outputs differ"
     assert torch.equal(lf, lu), f"{name}: fused and two-kernel lse differ"
     R = oracle.relproj(inp["r"], inp["P"], per_head=ph)
@@ -136,8 +139,9 @@ def test_fused_persistent_rounds_bitwise(B, Sq, Hq, Hkv, window):
     w = scaled(CONFIGS["c2_swa_prefill"], B=B, Sq=Sq, Skv=Sq, Hq=Hq, Hkv=Hkv, window=window)
     say(f"fused rounds: {w}")
     d = {k: v.to(DEV) for k, v in make_inputs(w).items()}
-    (of, lf), (ou, lu) = both_paths(d, w, d["r"], False)
-    assert torch.equal(of, ou) and torch.equal(lf, lu)
+    for on_chip in (False, True):
+        (of, lf), (ou, lu) = both_paths(d, w, d["r"], False, on_chip)
+        assert torch.equal(of, ou) and torch.equal(lf, lu), f"on_chip={on_chip}"
 
 
 def test_fused_full_size_workload_bitwise_and_sampled():
@@ -149,6 +153,8 @@ def test_fused_full_size_workload_bitwise_and_sampled():
     d = {k: v.to(DEV) for k, v in inp.items()}
     (of, lf), (ou, lu) = both_paths(d, w, d["r"], False)
     assert torch.equal(of, ou) and torch.equal(lf, lu)
+    (oc, lc), _ = both_paths(d, w, d["r"], False, on_chip=True)
+    assert torch.equal(oc, ou) and torch.equal(lc, lu), "on-chip path"
     rows = [0, 31, 4095, 4096, 8191]
     R = oracle.relproj(inp["r"][:, rows], inp["P"])
     for i, t in enumerate(rows):
@@ -164,6 +170,8 @@ def test_fused_full_causal_workload_bitwise():
     d = {k: v.to(DEV) for k, v in make_inputs(w).items()}
     (of, lf), (ou, lu) = both_paths(d, w, d["r"], False)
     assert torch.equal(of, ou) and torch.equal(lf, lu)
+    (oc, lc), _ = both_paths(d, w, d["r"], False, on_chip=True)
+    assert torch.equal(oc, ou) and torch.equal(lc, lu), "on-chip path"
 
 
 def test_fused_workspace_checks_and_reuse():
@@ -181,9 +189,13 @@ def test_fused_workspace_checks_and_reuse():
     rb = m.make_relbias(d["r"], PT)
     small_ws = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
     st = m._stream(d["q"].device)
-    assert m._lib.rba_attn_prefill_fused(ctypes.byref(a), ctypes.byref(rb), None, 0, st) == m.RBA_E_WORKSPACE
     assert m._lib.rba_attn_prefill_fused(ctypes.byref(a), ctypes.byref(rb), ctypes.c_void_p(small_ws.data_ptr()),
                                          need - 16, st) == m.RBA_E_WORKSPACE
+    # no workspace at all: accepted (on-chip path) for r_dim <= 64, refused above
+    w128 = scaled(w, r_dim=128)
+    r128 = make_inputs(w128)["r"].to(DEV)
+    rb128 = m.make_relbias(r128, m.relproj_pack(make_inputs(w128)["P"].to(DEV)))
+    assert m._lib.rba_attn_prefill_fused(ctypes.byref(a), ctypes.byref(rb128), None, 0, st) == m.RBA_E_WORKSPACE
     ws = torch.full((need,), 0x7f, dtype=torch.uint8, device=DEV)   # NaN-like bf16 garbage
     o1 = m.attn_prefill_fused(d["q"], d["k"], d["v"], d["r"], PT, workspace=ws)
     # a different problem through the same workspace, then the first again
@@ -194,3 +206,27 @@ def test_fused_workspace_checks_and_reuse():
     ou = m.attn_prefill(d["q"], d["k"], d["v"], R)
     torch.cuda.synchronize()
     assert torch.equal(o1, ou) and torch.equal(o2, ou)
+
+
+def test_fused_on_chip_needs_no_workspace():
+    """r_dim <= 64 with no workspace: the relative logits go straight to LDS;
+    two calls in a row (different inputs, then the first again) each equal
+    the two-kernel path bit for bit."""
+    m = rba()
+    w = scaled(CONFIGS["c2_swa_prefill"], B=1, Sq=256, Skv=256, Hq=16, Hkv=2, window=0, E=64)
+    outs = []
+    for seed in (None, 5, None):
+        inp = make_inputs(w) if seed is None else make_inputs(w, seed=seed)
+        d = {k: v.to(DEV) for k, v in inp.items()}
+        PT = m.relproj_pack(d["P"])
+        o = torch.empty_like(d["q"])
+        a = m.make_args(d["q"], d["k"], d["v"], None, o, None)
+        a.E = w.E
+        rb = m.make_relbias(d["r"], PT)
+        assert m._lib.rba_attn_prefill_fused(ctypes.byref(a), ctypes.byref(rb), None, 0, m._stream(d["q"].device)) \
+            == m.RBA_OK
+        ou = m.attn_prefill(d["q"], d["k"], d["v"], m.relproj(d["r"], d["P"]))
+        torch.cuda.synchronize()
+        assert torch.equal(o, ou)
+        outs.append(o)
+    assert torch.equal(outs[0], outs[2])
