@@ -46,16 +46,20 @@ def log(*a):
 # (factors from a plain 1 GiB device copy under the same counters), keyed by leg and by the sha256
 # prefix of the kernel source the counters were taken on; any other source reports null.
 PROFILED_TRAFFIC = {
-    ("c3", "4bb384e9d4699580"): 6543443 * 1024 * 2 + 1049088 * 1024,
-    ("c2", "4bb384e9d4699580"): 508752 * 1024 * 2 + 131594 * 1024,
-    ("c4w/head-major", "4bb384e9d4699580"): 578560 * 1024 * 2 + 9216 * 1024,
-    ("c4f/head-major", "4bb384e9d4699580"): 1225728 * 1024 * 2 + 9216 * 1024,
-    ("c5/head-major", "4bb384e9d4699580"): 524484 * 1024 * 2 + 2064 * 1024,
-    ("c4f_paged64/head-major", "4bb384e9d4699580"): 1163403 * 1024 * 2 + 9218 * 1024,
-    ("c4f_mxfp8/head-major", "4bb384e9d4699580"): 654424 * 1024 * 2 + 9216 * 1024,
-    ("c4f_mxfp8_logits/head-major", "4bb384e9d4699580"): 654448 * 1024 * 2 + 9216 * 1024,
-    ("c5_mxfp8/head-major", "4bb384e9d4699580"): 270643 * 1024 * 2 + 2064 * 1024,
-    ("c5_mxfp8_logits/head-major", "4bb384e9d4699580"): 270647 * 1024 * 2 + 2064 * 1024,
+    ("c3", "ac1e0709a59684d1"): 6524513 * 1024 * 2 + 1049088 * 1024,
+    ("c2", "ac1e0709a59684d1"): 509021 * 1024 * 2 + 131593 * 1024,
+    ("c3_fused_on_chip", "ac1e0709a59684d1"): 2880876 * 1024 * 2 + 1048855 * 1024,
+    ("c2_fused_on_chip", "ac1e0709a59684d1"): 145319 * 1024 * 2 + 132937 * 1024,
+    ("c3_fused_workspace", "ac1e0709a59684d1"): 6329556 * 1024 * 2 + 5280502 * 1024,
+    ("c2_fused_workspace", "ac1e0709a59684d1"): 532242 * 1024 * 2 + 660137 * 1024,
+    ("c4w/head-major", "ac1e0709a59684d1"): 578556 * 1024 * 2 + 9216 * 1024,
+    ("c4f/head-major", "ac1e0709a59684d1"): 1225724 * 1024 * 2 + 9216 * 1024,
+    ("c5/head-major", "ac1e0709a59684d1"): 524484 * 1024 * 2 + 2064 * 1024,
+    ("c4f_paged64/head-major", "ac1e0709a59684d1"): 1163403 * 1024 * 2 + 9218 * 1024,
+    ("c4f_mxfp8/head-major", "ac1e0709a59684d1"): 654406 * 1024 * 2 + 9216 * 1024,
+    ("c4f_mxfp8_logits/head-major", "ac1e0709a59684d1"): 654449 * 1024 * 2 + 9216 * 1024,
+    ("c5_mxfp8/head-major", "ac1e0709a59684d1"): 270642 * 1024 * 2 + 2064 * 1024,
+    ("c5_mxfp8_logits/head-major", "ac1e0709a59684d1"): 270641 * 1024 * 2 + 2064 * 1024,
 }
 
 
@@ -462,7 +466,7 @@ def prefill_leg(rba, torch, name, leg, steps, warmup, cpu_budget, fixed_rows=())
            "timing": "step: wall clock over the timed steps after torch.cuda.synchronize; kernels: back-to-back "
                      "mean of C-ABI launches between HIP events after a clock warm-up"}
     del R
-    res["fused"] = fused_prefill_leg(rba, torch, w, d, reps, ms_attn + ms_rp)
+    res["fused"] = fused_prefill_leg(rba, torch, w, d, reps, ms_attn + ms_rp, leg)
     del d, o, a_attn
     torch.cuda.empty_cache()
     if cpu_budget > 0:
@@ -515,7 +519,7 @@ def tiny_leg(rba, torch, cpu_budget):
     return res
 
 
-def fused_prefill_leg(rba, torch, w, d, reps, two_kernel_ms):
+def fused_prefill_leg(rba, torch, w, d, reps, two_kernel_ms, leg):
     """rba_attn_prefill_fused on the same workload: relproj and attention in one
     launch, the rows of R kept in a per-workgroup workspace instead of HBM, and
     without a workspace (each banded key tile's logits computed into LDS)."""
@@ -537,8 +541,10 @@ def fused_prefill_leg(rba, torch, w, d, reps, two_kernel_ms):
            "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
            "two_kernel_ms": round(two_kernel_ms, 4), "speedup_vs_two_kernels": round(two_kernel_ms / ms, 4),
            "workspace_bytes": need, "kernel": "attn_prefill_pp_kernel<4> (rows of R per block in the workspace)",
+           "traffic": traffic(leg + "_fused_workspace"),
            "on_chip": {"ms": round(ms_oc, 4), "step_tflops": round(flops / (ms_oc * 1e-3) / 1e12, 1),
                        "speedup_vs_two_kernels": round(two_kernel_ms / ms_oc, 4), "workspace_bytes": 0,
+                       "traffic": traffic(leg + "_fused_on_chip"),
                        "kernel": "attn_prefill_pp_kernel<4, on-chip> (banded tiles' logits computed into LDS)"},
            "timing": "back-to-back mean after a clock warm-up"}
     del ws, o, PT
