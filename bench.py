@@ -363,9 +363,11 @@ def paged_decode_leg(rba, torch, name, page_size, reps, len_lo, seed=77):
     return res
 
 
-def prologue_leg(rba, torch, name, new_tokens, seq_lens, Skv, reps, mxfp8=False):
+def prologue_leg(rba, torch, name, new_tokens, seq_lens, Skv, reps, mxfp8=False, max_new=0):
     """The attention prologue (K/V ShortConv W=4, Q/K RMSNorm, cache write) for a
-    batch of new tokens with 64 query / 8 kv heads; HBM-bound."""
+    batch of new tokens with 64 query / 8 kv heads; HBM-bound.  max_new > 0 passes
+    that bound on the new tokens per sequence (one launch); the launch without it
+    (new tokens in chunks, a second launch for the conv states) is timed beside."""
     from workloads import make_prologue_inputs
     inp = make_prologue_inputs(new_tokens, seq_lens, Hq=64, Hkv=8, W=4)
     d = {k: v.to("cuda") for k, v in inp.items()}
@@ -383,7 +385,8 @@ def prologue_leg(rba, torch, name, new_tokens, seq_lens, Skv, reps, mxfp8=False)
     qo = torch.empty_like(d["q"])
     # the call once through the binding (checks), then the C entry point with prebuilt arguments
     rba.attn_prologue(d["q"], d["k"], d["v"], d["cu_new"], d["seq_lens"], d["conv_wk"], d["conv_wv"], d["norm_q"],
-                      d["norm_k"], d["state_k"], d["state_v"], kc, vc, k_scale=ks, v_scale=vs, q_out=qo)
+                      d["norm_k"], d["state_k"], d["state_v"], kc, vc, k_scale=ks, v_scale=vs, q_out=qo,
+                      max_new=max_new)
     a = rba._PrologueArgs()
     a.B, a.T, a.Hq, a.Hkv, a.d, a.conv_w, a.eps = B, T, 64, 8, 128, 4, 1e-6
     a.cu_new, a.seq_lens = d["cu_new"].data_ptr(), d["seq_lens"].data_ptr()
@@ -394,8 +397,14 @@ def prologue_leg(rba, torch, name, new_tokens, seq_lens, Skv, reps, mxfp8=False)
     a.norm_q, a.norm_k = d["norm_q"].data_ptr(), d["norm_k"].data_ptr()
     a.state_k, a.state_v, a.q_out = d["state_k"].data_ptr(), d["state_v"].data_ptr(), qo.data_ptr()
     c = rba.cache_args(kc, vc, k_scale=ks, v_scale=vs)
+    a.max_new = max_new
     launch = c_launcher(rba, "rba_attn_prologue", ctypes.byref(a), ctypes.byref(c), None, rba._stream(qo.device))
     ms = time_launches(launch, reps, torch)
+    ms_chunked = None
+    if max_new > 0:
+        a.max_new = 0
+        ms_chunked = time_launches(launch, reps, torch)
+        a.max_new = max_new
     row = 128 * 2
     kv_row = 132 if mxfp8 else row
     # q, k, v read once; conv-state rows read and written; q_out and the cache rows written
@@ -404,6 +413,10 @@ def prologue_leg(rba, torch, name, new_tokens, seq_lens, Skv, reps, mxfp8=False)
            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": nbytes, "tokens": T,
            "cache": ("MXFP8" if mxfp8 else "bf16") + ", head-major [B, Hkv, Skv, d] storage",
            "timing": "back-to-back mean after a clock warm-up"}
+    if max_new > 0:
+        res["max_new"] = max_new
+        res["launches"] = "one (K/V rows of a sequence in order per half wave, conv state advanced in place)"
+        res["chunked_ms"] = round(ms_chunked, 4)
     del d, kc, vc, ks, vs, qo
     torch.cuda.empty_cache()
     return res
@@ -650,8 +663,9 @@ def main():
         log("attention prologue ...")
         out["prologue"] = {
             "prefill_8192": prologue_leg(rba, torch, "prefill", [8192], [8192], 8192, 20),
-            "decode_64x9": prologue_leg(rba, torch, "decode", [9] * 64, [9216] * 64, 9216, 50),
-            "decode_64x9_mxfp8": prologue_leg(rba, torch, "decode", [9] * 64, [9216] * 64, 9216, 50, mxfp8=True),
+            "decode_64x9": prologue_leg(rba, torch, "decode", [9] * 64, [9216] * 64, 9216, 50, max_new=9),
+            "decode_64x9_mxfp8": prologue_leg(rba, torch, "decode", [9] * 64, [9216] * 64, 9216, 50, mxfp8=True,
+                                              max_new=9),
         }
     if "attainable" in legs:
         att = attainable(rba, torch)

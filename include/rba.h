@@ -310,7 +310,16 @@ rba_status rba_mxfp8_quantize(rba_dtype in_dt, int64_t rows, int n, const void *
  * fields are ignored.  MXFP8 caches receive the bf16 row encoded as by
  * rba_mxfp8_quantize.  `paged` (NULL = dense [B, Skv, Hkv, d]) selects a
  * block-table cache as for rba_attn_paged.  d = 128, 1 <= conv_w <= 8,
- * eps > 0.  T = 0 is a no-op.                                              */
+ * eps > 0.  T = 0 is a no-op.
+ *   max_new    : 0, or a bound on every n_b.  With 1 <= max_new <= 32 the
+ *                prologue is one launch in which each sequence's K and V rows
+ *                are taken in order by one half wave per kv head, which also
+ *                advances that sequence's conv state (decode and MTP verify
+ *                batches); otherwise new tokens are taken in chunks of 8 and
+ *                a second launch advances the states.  Both give the same
+ *                bits; a bound that a sequence exceeds is not an error (its
+ *                tokens are all still taken, only more slowly).  < 0 is
+ *                RBA_E_INVALID.                                           */
 typedef struct rba_prologue_args {
     int B, T, Hq, Hkv, d;
     int conv_w;
@@ -324,6 +333,7 @@ typedef struct rba_prologue_args {
     void *state_k, *state_v;
     void *q_out;
     int64_t q_out_s[2];
+    int max_new;
 } rba_prologue_args;
 
 rba_status rba_attn_prologue(const rba_prologue_args *args, const rba_attn_args *cache, const rba_paged_kv *paged,

@@ -83,6 +83,7 @@ class _PrologueArgs(ctypes.Structure):
         ("state_k", ctypes.c_void_p), ("state_v", ctypes.c_void_p),
         ("q_out", ctypes.c_void_p),
         ("q_out_s", ctypes.c_int64 * 2),
+        ("max_new", ctypes.c_int),
     ]
 
 
@@ -482,11 +483,13 @@ def cache_args(k_cache, v_cache, *, k_scale=None, v_scale=None, max_seq_len=None
 
 
 def attn_prologue(q, k, v, cu_new, seq_lens, conv_wk, conv_wv, norm_q, norm_k, state_k, state_v, k_cache, v_cache,
-                  *, eps=1e-6, k_scale=None, v_scale=None, block_table=None, max_seq_len=None, q_out=None):
+                  *, eps=1e-6, k_scale=None, v_scale=None, block_table=None, max_seq_len=None, q_out=None,
+                  max_new=0):
     """Attention prologue for T new tokens: returns q_out = RMSNorm(q) and writes
     RMSNorm(ShortConv(k)) and ShortConv(v) into the cache at each sequence's new
     positions, then advances the conv states (see rba.h for the layouts).
-    block_table (int32 [B, n]) makes k_cache / v_cache page pools."""
+    block_table (int32 [B, n]) makes k_cache / v_cache page pools.  max_new (a
+    bound on any sequence's new tokens, 0 = none) selects the one-launch path."""
     T, Hq, d = q.shape
     W = conv_wk.shape[1]
     for t in (q, k, v, cu_new, seq_lens, conv_wk, conv_wv, norm_q, norm_k, k_cache, v_cache):
@@ -500,6 +503,7 @@ def attn_prologue(q, k, v, cu_new, seq_lens, conv_wk, conv_wv, norm_q, norm_k, s
     out = torch.empty(T, Hq, d, dtype=torch.bfloat16, device=q.device) if q_out is None else q_out
     a = _PrologueArgs()
     a.B, a.T, a.Hq, a.Hkv, a.d, a.conv_w, a.eps = seq_lens.shape[0], T, Hq, k.shape[1], d, W, float(eps)
+    a.max_new = int(max_new)
     a.cu_new, a.seq_lens = cu_new.data_ptr(), seq_lens.data_ptr()
     a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
     for name, t in (("q_s", q), ("k_s", k), ("v_s", v), ("q_out_s", out)):

@@ -63,6 +63,7 @@ __device__ __forceinline__ void rms_norm4(float x[4], const float g[4], float ep
 
 constexpr int TC = 8;          // consecutive tokens per half wave
 constexpr int kMaxTaps = 8;    // largest tap count
+constexpr int kSeqMaxNew = 32; // largest max_new served by the one-launch (per-sequence) kernel
 
 // The sequence owning token t: the last b with cu_new[b] <= t.
 __device__ __forceinline__ int seq_of(const int *cu, int B, int t) {
@@ -72,6 +73,53 @@ __device__ __forceinline__ int seq_of(const int *cu, int B, int t) {
         if (cu[mid] <= t) lo = mid; else hi = mid;
     }
     return lo;
+}
+
+// Writes one convolved (and for K normalised) row: this lane's 4 channels of
+// kv head g at cache position pos of sequence b, dense or through the block
+// table, as bf16 or as MXFP8 (eight lanes per 32-entry block share the block
+// maximum).
+template <bool F8, bool PG>
+__device__ __forceinline__ void write_cache_row(const PrologueParams &p, bool isk, int b, int pos, int g, int c0,
+                                                int lane, const float acc[4]) {
+    const int64_t cs0 = isk ? p.cks0 : p.cvs0, cs1 = isk ? p.cks1 : p.cvs1, cs2 = isk ? p.cks2 : p.cvs2;
+    const int64_t ss0 = isk ? p.sks0 : p.svs0, ss1 = isk ? p.sks1 : p.svs1, ss2 = isk ? p.sks2 : p.svs2;
+    int64_t off, soff;                    // element (= byte for MXFP8) and scale offsets of the row
+    if constexpr (PG) {
+        const int pg = pos / p.page_size;
+        const int page = min(max(p.block_table[(int64_t)b * p.bt_stride + pg], 0), p.num_pages - 1);
+        const int r = pos - pg * p.page_size;
+        off = (int64_t)page * cs0 + (int64_t)r * cs1 + (int64_t)g * cs2;
+        soff = (int64_t)page * ss0 + (int64_t)r * ss1 + (int64_t)g * ss2;
+    } else {
+        off = (int64_t)b * cs0 + (int64_t)pos * cs1 + (int64_t)g * cs2;
+        soff = (int64_t)b * ss0 + (int64_t)pos * ss1 + (int64_t)g * ss2;
+    }
+    const u32x2 h = pack4(acc);
+    if constexpr (!F8) {
+        *(u32x2 *)((__bf16 *)(isk ? p.k_cache : p.v_cache) + off + c0) = h;
+    } else {
+        // encode the bf16 row: block = 8 lanes (32 entries)
+        float y[4];
+        y[0] = __builtin_bit_cast(float, h[0] << 16);
+        y[1] = __builtin_bit_cast(float, h[0] & 0xffff0000u);
+        y[2] = __builtin_bit_cast(float, h[1] << 16);
+        y[3] = __builtin_bit_cast(float, h[1] & 0xffff0000u);
+        float amax = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        amax = fmaxf(amax, __shfl_xor(amax, 4));
+        int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 1 - 8 : -127;
+        ex = min(max(ex, -127), 127);
+        float sc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[j] = fminf(fmaxf(ldexpf(y[j], -ex), -448.f), 448.f);
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(sc[0], sc[1], 0, false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(sc[2], sc[3], wd, true);
+        *(unsigned *)((uint8_t *)(isk ? p.k_cache : p.v_cache) + off + c0) = (unsigned)wd;
+        if ((lane & 7) == 0)
+            ((uint8_t *)(isk ? p.k_scale : p.v_scale))[soff + (lane >> 3)] = (uint8_t)(ex + 127);
+    }
 }
 
 // Half a wave owns one head row kind (q head, k head or v head) for TC
@@ -129,9 +177,6 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrologueParams p) {
             gk[e] = isk ? p.norm_k[c0 + e] : 1.f;
         }
     }
-    const int64_t cs0 = isk ? p.cks0 : p.cvs0, cs1 = isk ? p.cks1 : p.cvs1, cs2 = isk ? p.cks2 : p.cvs2;
-    const int64_t ss0 = isk ? p.sks0 : p.svs0, ss1 = isk ? p.sks1 : p.svs1, ss2 = isk ? p.sks2 : p.svs2;
-
     float hist[WMAX - 1][4];                  // hist[l - 1] = pre-convolution row l positions back
     int b = -1, a0 = 0, a1 = 0, n = 0, L = 0;
 #pragma unroll
@@ -179,43 +224,150 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrologueParams p) {
         for (int e = 0; e < 4; ++e) hist[0][e] = x[e];
         if (isk) rms_norm4(acc, gk, p.eps);
 
-        // destination row of the cache
-        int64_t off, soff;                    // element (= byte for MXFP8) and scale offsets of the row
-        if constexpr (PG) {
-            const int pg = pos / p.page_size;
-            const int page = min(max(p.block_table[(int64_t)b * p.bt_stride + pg], 0), p.num_pages - 1);
-            const int r = pos - pg * p.page_size;
-            off = (int64_t)page * cs0 + (int64_t)r * cs1 + (int64_t)g * cs2;
-            soff = (int64_t)page * ss0 + (int64_t)r * ss1 + (int64_t)g * ss2;
-        } else {
-            off = (int64_t)b * cs0 + (int64_t)pos * cs1 + (int64_t)g * cs2;
-            soff = (int64_t)b * ss0 + (int64_t)pos * ss1 + (int64_t)g * ss2;
-        }
-        const u32x2 h = pack4(acc);
-        if constexpr (!F8) {
-            *(u32x2 *)((__bf16 *)(isk ? p.k_cache : p.v_cache) + off + c0) = h;
-        } else {
-            // encode the bf16 row: block = 8 lanes (32 entries)
-            float y[4];
-            y[0] = __builtin_bit_cast(float, h[0] << 16);
-            y[1] = __builtin_bit_cast(float, h[0] & 0xffff0000u);
-            y[2] = __builtin_bit_cast(float, h[1] << 16);
-            y[3] = __builtin_bit_cast(float, h[1] & 0xffff0000u);
-            float amax = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
-            amax = fmaxf(amax, __shfl_xor(amax, 1));
-            amax = fmaxf(amax, __shfl_xor(amax, 2));
-            amax = fmaxf(amax, __shfl_xor(amax, 4));
-            int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 1 - 8 : -127;
-            ex = min(max(ex, -127), 127);
-            float sc[4];
+        write_cache_row<F8, PG>(p, isk, b, pos, g, c0, lane, acc);
+    }
+}
+
+// One launch for batches whose sequences each bring few new tokens (the
+// caller's bound max_new: decode and MTP verify).  q rows are normalised per
+// chunk of TC tokens as in prologue_kernel; for K and V, half a wave owns one
+// stream and kv head of one sequence and takes all of that sequence's new
+// tokens in order, TC at a time.  It is then the only reader of the sequence's conv
+// state for its stream and kv head, so it also advances that state itself
+// (the rows of the sequence's last W-1 positions, old rows kept verbatim), and
+// no second kernel is needed.  All of its loads except the rows of later
+// chunks are issued together at the start.
+template <bool F8, bool PG, int WMAX>
+__global__ __launch_bounds__(256) void prologue_seq_kernel(const PrologueParams p) {
+    const int64_t item = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+    const int lane = threadIdx.x & 31;
+    const int c0 = 4 * lane;
+    // items: (chunk of TC tokens, q head) first, as in prologue_kernel, then
+    // (sequence, k or v, kv head)
+    const int64_t nq = (int64_t)((p.T + TC - 1) / TC) * p.Hq;
+    if (item < nq) {                          // q: RMSNorm only
+        const int chunk = (int)(item / p.Hq);
+        const int hq = (int)(item - (int64_t)chunk * p.Hq);
+        const int t0 = chunk * TC, t1 = min(p.T, t0 + TC);
+        const __bf16 *srow = p.q + (int64_t)hq * p.qs1 + c0;
+        u32x2 raw[TC];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sc[j] = fminf(fmaxf(ldexpf(y[j], -ex), -448.f), 448.f);
-            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(sc[0], sc[1], 0, false);
-            wd = __builtin_amdgcn_cvt_pk_fp8_f32(sc[2], sc[3], wd, true);
-            *(unsigned *)((uint8_t *)(isk ? p.k_cache : p.v_cache) + off + c0) = (unsigned)wd;
-            if ((lane & 7) == 0)
-                ((uint8_t *)(isk ? p.k_scale : p.v_scale))[soff + (lane >> 3)] = (uint8_t)(ex + 127);
+        for (int j = 0; j < TC; ++j) raw[j] = t0 + j < t1 ? *(const u32x2 *)(srow + (int64_t)(t0 + j) * p.qs0) : u32x2{0u, 0u};
+        float gq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gq[e] = p.norm_q[c0 + e];
+#pragma unroll
+        for (int j = 0; j < TC; ++j) {
+            if (t0 + j >= t1) break;
+            float x[4];
+            unpack4(raw[j], x);
+            rms_norm4(x, gq, p.eps);
+            *(u32x2 *)(p.q_out + (int64_t)(t0 + j) * p.qos0 + (int64_t)hq * p.qos1 + c0) = pack4(x);
         }
+        return;
+    }
+    const int64_t kvi = item - nq;
+    if (kvi >= (int64_t)p.B * 2 * p.Hkv) return;   // the whole half wave leaves together
+    const int b = (int)(kvi / (2 * p.Hkv));
+    const int hr = (int)(kvi - (int64_t)b * 2 * p.Hkv);
+    const bool isk = hr < p.Hkv;
+    const int g = isk ? hr : hr - p.Hkv;
+    // device values clamped so that every access stays in its tensor
+    const int a0 = min(max(p.cu_new[b], 0), p.T);
+    const int a1 = min(max(p.cu_new[b + 1], a0), p.T);
+    const int n = a1 - a0;
+    const int L = min(max(p.seq_lens[b], n), p.Skv);
+    const int64_t s0 = isk ? p.ks0 : p.vs0;
+    const __bf16 *srow = (isk ? p.k : p.v) + (int64_t)g * (isk ? p.ks1 : p.vs1) + c0;
+
+    if (n == 0) return;                       // no new rows: cache and state unchanged
+    __bf16 *const state = isk ? p.state_k : p.state_v;
+    const int W = p.W;
+    const int64_t st_b = (int64_t)b * (W - 1);   // first state row of this sequence
+    auto state_row = [&](int r) __attribute__((always_inline)) { return state + ((st_b + r) * p.Hkv + g) * D + c0; };
+
+    // loads issued together: the old state rows (verbatim), the new rows that
+    // end up in the advanced state, the taps and norm weight, the first chunk
+    u32x2 old[WMAX - 1], keep[WMAX - 1];
+#pragma unroll
+    for (int r = 0; r < WMAX - 1; ++r) old[r] = r < W - 1 ? *(const u32x2 *)state_row(r) : u32x2{0u, 0u};
+    // advanced state row j = pre-convolution row of position L - (W-1) + j:
+    // old row n + j while n + j < W - 1, else new row a0 + n + j - (W - 1)
+#pragma unroll
+    for (int j = 0; j < WMAX - 1; ++j) {
+        const int k = n + j;
+        keep[j] = (j < W - 1 && k >= W - 1) ? *(const u32x2 *)(srow + (int64_t)(a0 + k - (W - 1)) * s0)
+                                            : u32x2{0u, 0u};
+    }
+    float w[4][WMAX], gk[4];
+    {
+        const float *wp = (isk ? p.conv_wk : p.conv_wv) + (int64_t)(g * D + c0) * W;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int l = 0; l < WMAX; ++l) w[e][l] = l < W ? wp[e * W + l] : 0.f;
+            gk[e] = isk ? p.norm_k[c0 + e] : 1.f;
+        }
+    }
+    u32x2 raw[TC];
+#pragma unroll
+    for (int j = 0; j < TC; ++j) raw[j] = a0 + j < a1 ? *(const u32x2 *)(srow + (int64_t)(a0 + j) * s0) : u32x2{0u, 0u};
+
+    // history of the first new token: row l positions back is old row
+    // W - 1 - l, zero before the sequence's first position
+    float hist[WMAX - 1][4];
+#pragma unroll
+    for (int l = 1; l < WMAX; ++l) {
+        u32x2 v = u32x2{0u, 0u};
+#pragma unroll
+        for (int r = 0; r < WMAX - 1; ++r)
+            if (r == W - 1 - l) v = old[r];
+        if (!(l < W && L - n - l >= 0)) v = u32x2{0u, 0u};
+        unpack4(v, hist[l - 1]);
+    }
+
+    for (int t0 = a0; t0 < a1; t0 += TC) {
+        if (t0 > a0) {
+#pragma unroll
+            for (int j = 0; j < TC; ++j)
+                raw[j] = t0 + j < a1 ? *(const u32x2 *)(srow + (int64_t)(t0 + j) * s0) : u32x2{0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < TC; ++j) {
+            const int t = t0 + j;
+            if (t >= a1) break;
+            const int pos = L - n + (t - a0);
+            float x[4], acc[4];
+            unpack4(raw[j], x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] = w[e][0] * x[e];
+#pragma unroll
+                for (int l = 1; l < WMAX; ++l) acc[e] = fmaf(w[e][l], hist[l - 1][e], acc[e]);
+            }
+#pragma unroll
+            for (int l = WMAX - 2; l > 0; --l)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hist[l][e] = hist[l - 1][e];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hist[0][e] = x[e];
+            if (isk) rms_norm4(acc, gk, p.eps);
+            write_cache_row<F8, PG>(p, isk, b, pos, g, c0, lane, acc);
+        }
+    }
+
+    // advance the state (every read of the old rows is done above)
+#pragma unroll
+    for (int j = 0; j < WMAX - 1; ++j) {
+        if (j >= W - 1) break;
+        const int k = n + j;
+        u32x2 v = keep[j];
+        if (k < W - 1) {
+#pragma unroll
+            for (int r = 0; r < WMAX - 1; ++r)
+                if (r == k) v = old[r];
+        }
+        *(u32x2 *)state_row(j) = v;
     }
 }
 
@@ -251,6 +403,26 @@ __global__ __launch_bounds__(256) void conv_state_kernel(const PrologueParams p)
 }  // namespace
 
 hipError_t launch_prologue(const PrologueParams &p, hipStream_t stream) {
+    if (p.max_new >= 1 && p.max_new <= kSeqMaxNew && p.B > 0) {
+        // one launch: a half wave per (sequence, head row kind)
+        const int64_t items = (int64_t)((p.T + TC - 1) / TC) * p.Hq + (int64_t)p.B * 2 * p.Hkv;
+        const int64_t grid = (items + 7) / 8;
+        if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+        const bool f8 = p.k_scale != nullptr, pg = p.block_table != nullptr, w4 = p.W <= 4;
+#define RBA_PROS(F8, PG, WM) \
+    hipLaunchKernelGGL((prologue_seq_kernel<F8, PG, WM>), dim3((unsigned)grid), dim3(256), 0, stream, p)
+        if (f8 && pg) {
+            if (w4) RBA_PROS(true, true, 4); else RBA_PROS(true, true, kMaxTaps);
+        } else if (f8) {
+            if (w4) RBA_PROS(true, false, 4); else RBA_PROS(true, false, kMaxTaps);
+        } else if (pg) {
+            if (w4) RBA_PROS(false, true, 4); else RBA_PROS(false, true, kMaxTaps);
+        } else {
+            if (w4) RBA_PROS(false, false, 4); else RBA_PROS(false, false, kMaxTaps);
+        }
+#undef RBA_PROS
+        return hipGetLastError();
+    }
     const int64_t items = (int64_t)((p.T + TC - 1) / TC) * (p.Hq + 2 * p.Hkv);
     if (items > 0) {
         const int64_t grid = (items + 7) / 8;

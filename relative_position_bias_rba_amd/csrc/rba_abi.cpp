@@ -375,6 +375,7 @@ rba_status rba_attn_prologue(const rba_prologue_args *a, const rba_attn_args *c,
     if (a->B < 0 || a->T < 0 || a->Hq < 1 || a->Hkv < 1 || a->Hkv != c->Hkv || c->Skv < 1) return RBA_E_INVALID;
     if (a->conv_w < 1 || a->conv_w > kMaxConvTaps) return RBA_E_INVALID;
     if (!isfinite(a->eps) || !(a->eps > 0.f)) return RBA_E_INVALID;
+    if (a->max_new < 0) return RBA_E_INVALID;
     if (a->T == 0) return RBA_OK;
     if (a->B < 1) return RBA_E_INVALID;
     if (a->cu_new == nullptr || a->seq_lens == nullptr || a->q == nullptr || a->k == nullptr || a->v == nullptr ||
@@ -409,6 +410,7 @@ rba_status rba_attn_prologue(const rba_prologue_args *a, const rba_attn_args *c,
     rba::PrologueParams p{};
     p.B = a->B, p.T = a->T, p.Hq = a->Hq, p.Hkv = a->Hkv, p.W = a->conv_w, p.Skv = c->Skv;
     p.eps = a->eps;
+    p.max_new = a->max_new;
     p.cu_new = a->cu_new, p.seq_lens = a->seq_lens;
     p.q = (const __bf16 *)a->q, p.k = (const __bf16 *)a->k, p.v = (const __bf16 *)a->v;
     p.qs0 = a->q_s[0], p.qs1 = a->q_s[1], p.ks0 = a->k_s[0], p.ks1 = a->k_s[1];

@@ -72,6 +72,7 @@ struct PrologueParams {
     const int *block_table;                    // paged cache when != null
     int64_t bt_stride;
     int page_size, num_pages;
+    int max_new;                               // bound on any sequence's new tokens (0 = none given)
 };
 
 hipError_t launch_prologue(const PrologueParams &p, hipStream_t stream);

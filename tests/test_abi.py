@@ -290,6 +290,7 @@ def test_prologue_validation():
         (lambda a, c: setattr(a, "conv_w", 9), RBA_E_INVALID),
         (lambda a, c: setattr(a, "eps", 0.0), RBA_E_INVALID),
         (lambda a, c: setattr(a, "eps", float("inf")), RBA_E_INVALID),
+        (lambda a, c: setattr(a, "max_new", -1), RBA_E_INVALID),
         (lambda a, c: setattr(a, "Hkv", 3), RBA_E_INVALID),
         (lambda a, c: setattr(a, "B", 0), RBA_E_INVALID),
         (lambda a, c: setattr(a, "cu_new", None), RBA_E_INVALID),

@@ -42,9 +42,11 @@ def close(name, got, want):
     assert not bad.any(), f"{name}: {bad.sum()} entries off, first {np.argwhere(bad)[:3].tolist()}"
 
 
-def run(inp, Skv, *, f8=False, paged=None, W=None, head_major=False):
+def run(inp, Skv, *, f8=False, paged=None, W=None, head_major=False, max_new=0):
     """head_major: the dense cache is stored [B, Hkv, Skv, ...] and passed as a
-    [B, Skv, Hkv, ...] view with those strides."""
+    [B, Skv, Hkv, ...] view with those strides.  max_new: the bound on new tokens
+    per sequence passed to the library (0: none; 1..32 selects the one-launch
+    path, which must stay exact when a sequence exceeds the bound)."""
     m = rba()
     d = {k: v.to(DEV) for k, v in inp.items()}
     B = d["seq_lens"].shape[0]
@@ -73,7 +75,8 @@ def run(inp, Skv, *, f8=False, paged=None, W=None, head_major=False):
     sk, sv = d["state_k"].clone(), d["state_v"].clone()
     qo = m.attn_prologue(d["q"], d["k"], d["v"], d["cu_new"], d["seq_lens"], d["conv_wk"], d["conv_wv"],
                          d["norm_q"], d["norm_k"], sk if sk.numel() else None, sv if sv.numel() else None, kc, vc,
-                         eps=1e-6, k_scale=ks, v_scale=vs, block_table=table, max_seq_len=Skv if paged else None)
+                         eps=1e-6, k_scale=ks, v_scale=vs, block_table=table, max_seq_len=Skv if paged else None,
+                         max_new=max_new)
     torch.cuda.synchronize()
     return qo, kc, vc, ks, vs, sk, sv
 
@@ -94,11 +97,12 @@ def seq_of(inp):
 MIX = dict(new=[1, 9, 37, 20, 2], lens=[500, 9, 37, 100, 2])
 
 
+@pytest.mark.parametrize("max_new", [0, 32, 1], ids=["chunked", "one_launch", "bound_exceeded"])
 @pytest.mark.parametrize("W", [4, 2, 1])
-def test_prologue_dense_bf16(W):
-    say(f"prologue dense W={W}")
+def test_prologue_dense_bf16(W, max_new):
+    say(f"prologue dense W={W} max_new={max_new}")
     inp = make_prologue_inputs(MIX["new"], MIX["lens"], Hq=16, Hkv=2, W=W)
-    qo, kc, vc, _, _, sk, sv = run(inp, 512)
+    qo, kc, vc, _, _, sk, sv = run(inp, 512, max_new=max_new)
     q_o, k_o, v_o, pos, nsk, nsv = oracle_of(inp)
     close("q_out", qo, q_o)
     bs = seq_of(inp)
@@ -199,7 +203,8 @@ def test_prologue_mxfp8_cache():
         assert ok.all(), f"{name}: {np.sum(~ok)} entries off"
 
 
-def test_prologue_ignores_garbage_state_before_sequence_start():
+@pytest.mark.parametrize("max_new", [0, 32], ids=["chunked", "one_launch"])
+def test_prologue_ignores_garbage_state_before_sequence_start(max_new):
     """Conv-state rows of positions before a sequence's start hold large
     garbage here (the generator zeroes them; a serving engine need not): the
     rows the call writes must not depend on them.  The oracle of the same
@@ -220,7 +225,7 @@ def test_prologue_ignores_garbage_state_before_sequence_start():
                 garbage["state_v"][b, j] = (torch.randn(2, 128, generator=g) * 300).to(torch.bfloat16)
                 n_garbage += 1
     assert n_garbage >= 6          # the two sequences that start inside the call, and the 2-token one
-    qo, kc, vc, _, _, sk, sv = run(garbage, 512)
+    qo, kc, vc, _, _, sk, sv = run(garbage, 512, max_new=max_new)
     q_o, k_o, v_o, pos_g, nsk, nsv = oracle_of(garbage)
     assert np.array_equal(pos, pos_g)
     assert np.allclose(k_o, clean_k, rtol=0, atol=0) and np.allclose(v_o, clean_v, rtol=0, atol=0)
@@ -229,3 +234,37 @@ def test_prologue_ignores_garbage_state_before_sequence_start():
     close("k rows (garbage state)", kc[bs, pos], clean_k)
     close("v rows (garbage state)", vc[bs, pos], clean_v)
     assert np.array_equal(sk.double().cpu().numpy(), nsk) and np.array_equal(sv.double().cpu().numpy(), nsv)
+
+
+@pytest.mark.parametrize("case", ["bf16", "mxfp8", "paged", "W8", "W1"])
+def test_prologue_one_launch_equals_chunked(case):
+    """With a bound on the new tokens per sequence the prologue runs as one
+    launch (K/V rows of a sequence taken in order by one half wave, which also
+    advances its conv state); without it, in chunks of 8 tokens plus a launch
+    for the states.  The arithmetic is the same, so every output (q_out, cache
+    rows and scales, untouched sentinels, conv states) must agree bit for bit,
+    here on a decode/verify batch (64 sequences of 9 tokens, the bound met) and
+    on the mixed batch with the bound exceeded."""
+    W = 8 if case == "W8" else (1 if case == "W1" else 4)
+    f8 = case == "mxfp8"
+    for new, lens, bound in (([9] * 64, [700 + 3 * b for b in range(64)], 9), (MIX["new"], MIX["lens"], 8)):
+        say(f"prologue one launch vs chunked: {case}, B={len(new)}, bound {bound}")
+        inp = make_prologue_inputs(new, lens, Hq=16, Hkv=2, W=W, seed=31)
+        paged = None
+        Skv = 1024
+        if case == "paged":
+            g = torch.Generator().manual_seed(3)
+            n_pages = 16 * len(new) + 1
+            table = torch.randperm(n_pages, generator=g)[:16 * len(new)].reshape(len(new), 16).to(torch.int32)
+            paged = (64, n_pages, table)
+        a = run(inp, Skv, f8=f8, paged=paged, max_new=0)
+        b = run(inp, Skv, f8=f8, paged=paged, max_new=bound)
+        for x, y in zip(a, b):
+            if x is not None:
+                assert torch.equal(x, y)
+        if not f8:
+            q_o, k_o, v_o, pos, nsk, nsv = oracle_of(inp)
+            close("q_out", b[0], q_o)
+            if W > 1:
+                assert np.array_equal(b[5].double().cpu().numpy(), nsk)
+                assert np.array_equal(b[6].double().cpu().numpy(), nsv)
