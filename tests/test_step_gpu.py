@@ -27,8 +27,9 @@ def say(*a):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("window,log_base,splits", [(0, 0.0, 0), (256, 0.0, 3), (0, 4096.0, 1)])
-def test_decode_step_prologue_then_paged_attention(window, log_base, splits):
+@pytest.mark.parametrize("window,log_base,splits,max_new", [(0, 0.0, 0, 0), (256, 0.0, 3, 9), (0, 4096.0, 1, 9)])
+def test_decode_step_prologue_then_paged_attention(window, log_base, splits, max_new):
+    """max_new = 9 runs the prologue as one launch (the bound the step knows)."""
     import relative_position_bias_rba_amd as rba
     Hq, Hkv, d, E, r_dim, ps = 16, 2, 128, 64, 32, 64
     new = [9, 9, 9]
@@ -55,7 +56,7 @@ def test_decode_step_prologue_then_paged_attention(window, log_base, splits):
     kp, vp, tb = k_pool.to(DEV), v_pool.to(DEV), table.to(DEV)
     q_out = rba.attn_prologue(dev["q"], dev["k"], dev["v"], dev["cu_new"], dev["seq_lens"], dev["conv_wk"],
                               dev["conv_wv"], dev["norm_q"], dev["norm_k"], dev["state_k"], dev["state_v"], kp, vp,
-                              block_table=tb, max_seq_len=Skv)
+                              block_table=tb, max_seq_len=Skv, max_new=max_new)
     R = rba.relproj(r.to(DEV), P.to(DEV))
     o = rba.attn_paged(q_out.reshape(B, 9, Hq, d), kp, vp, tb, dev["seq_lens"], R, max_seq_len=Skv,
                        window=window, log_scale_base=log_base, num_splits=splits)
