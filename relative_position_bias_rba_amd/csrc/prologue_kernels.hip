@@ -64,6 +64,7 @@ __device__ __forceinline__ void rms_norm4(float x[4], const float g[4], float ep
 constexpr int TC = 8;          // consecutive tokens per half wave
 constexpr int kMaxTaps = 8;    // largest tap count
 constexpr int kSeqMaxNew = 32; // largest max_new served by the one-launch (per-sequence) kernel
+constexpr int TCS = 16;        // new K/V rows per load batch of the one-launch kernel (a verify batch in one)
 
 // The sequence owning token t: the last b with cu_new[b] <= t.
 __device__ __forceinline__ int seq_of(const int *cu, int B, int t) {
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrologueParams p) {
 // caller's bound max_new: decode and MTP verify).  q rows are normalised per
 // chunk of TC tokens as in prologue_kernel; for K and V, half a wave owns one
 // stream and kv head of one sequence and takes all of that sequence's new
-// tokens in order, TC at a time.  It is then the only reader of the sequence's conv
+// tokens in order, TCS at a time.  It is then the only reader of the sequence's conv
 // state for its stream and kv head, so it also advances that state itself
 // (the rows of the sequence's last W-1 positions, old rows kept verbatim), and
 // no second kernel is needed.  All of its loads except the rows of later
@@ -309,9 +310,9 @@ __global__ __launch_bounds__(256) void prologue_seq_kernel(const PrologueParams 
             gk[e] = isk ? p.norm_k[c0 + e] : 1.f;
         }
     }
-    u32x2 raw[TC];
+    u32x2 raw[TCS];
 #pragma unroll
-    for (int j = 0; j < TC; ++j) raw[j] = a0 + j < a1 ? *(const u32x2 *)(srow + (int64_t)(a0 + j) * s0) : u32x2{0u, 0u};
+    for (int j = 0; j < TCS; ++j) raw[j] = a0 + j < a1 ? *(const u32x2 *)(srow + (int64_t)(a0 + j) * s0) : u32x2{0u, 0u};
 
     // history of the first new token: row l positions back is old row
     // W - 1 - l, zero before the sequence's first position
@@ -326,14 +327,14 @@ __global__ __launch_bounds__(256) void prologue_seq_kernel(const PrologueParams 
         unpack4(v, hist[l - 1]);
     }
 
-    for (int t0 = a0; t0 < a1; t0 += TC) {
+    for (int t0 = a0; t0 < a1; t0 += TCS) {
         if (t0 > a0) {
 #pragma unroll
-            for (int j = 0; j < TC; ++j)
+            for (int j = 0; j < TCS; ++j)
                 raw[j] = t0 + j < a1 ? *(const u32x2 *)(srow + (int64_t)(t0 + j) * s0) : u32x2{0u, 0u};
         }
 #pragma unroll
-        for (int j = 0; j < TC; ++j) {
+        for (int j = 0; j < TCS; ++j) {
             const int t = t0 + j;
             if (t >= a1) break;
             const int pos = L - n + (t - a0);
