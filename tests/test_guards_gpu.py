@@ -85,20 +85,22 @@ def test_paged_mxfp8_and_prologue_are_deterministic():
         assert torch.equal(x, y)
     pi = make_prologue_inputs([1, 9, 20], [300, 9, 100], Hq=16, Hkv=2, W=4)
     pd = {k: v.to(DEV) for k, v in pi.items()}
-    res = []
-    for _ in range(2):
-        kcache = torch.zeros(3, 320, 2, 128, dtype=torch.bfloat16, device=DEV)
-        vcache = torch.zeros_like(kcache)
-        sk, sv = pd["state_k"].clone(), pd["state_v"].clone()
-        qo = m.attn_prologue(pd["q"], pd["k"], pd["v"], pd["cu_new"], pd["seq_lens"], pd["conv_wk"],
-                             pd["conv_wv"], pd["norm_q"], pd["norm_k"], sk, sv, kcache, vcache)
-        res.append((qo, kcache, vcache, sk, sv))
-    torch.cuda.synchronize()
-    for x, y in zip(*res):
-        assert torch.equal(x, y)
+    for max_new in (0, 20):          # chunked, and one launch
+        res = []
+        for _ in range(2):
+            kcache = torch.zeros(3, 320, 2, 128, dtype=torch.bfloat16, device=DEV)
+            vcache = torch.zeros_like(kcache)
+            sk, sv = pd["state_k"].clone(), pd["state_v"].clone()
+            qo = m.attn_prologue(pd["q"], pd["k"], pd["v"], pd["cu_new"], pd["seq_lens"], pd["conv_wk"],
+                                 pd["conv_wv"], pd["norm_q"], pd["norm_k"], sk, sv, kcache, vcache, max_new=max_new)
+            res.append((qo, kcache, vcache, sk, sv))
+        torch.cuda.synchronize()
+        for x, y in zip(*res):
+            assert torch.equal(x, y)
 
 
-def test_prologue_writes_stay_inside_their_buffers():
+@pytest.mark.parametrize("max_new", [0, 20], ids=["chunked", "one_launch"])
+def test_prologue_writes_stay_inside_their_buffers(max_new):
     m = rba()
     pi = make_prologue_inputs([1, 9, 20], [300, 9, 100], Hq=16, Hkv=2, W=4, seed=5)
     pd = {k: v.to(DEV) for k, v in pi.items()}
@@ -110,7 +112,7 @@ def test_prologue_writes_stay_inside_their_buffers():
     sk.copy_(pd["state_k"])
     sv.copy_(pd["state_v"])
     m.attn_prologue(pd["q"], pd["k"], pd["v"], pd["cu_new"], pd["seq_lens"], pd["conv_wk"], pd["conv_wv"],
-                    pd["norm_q"], pd["norm_k"], sk, sv, kcache, vcache, q_out=qo)
+                    pd["norm_q"], pd["norm_k"], sk, sv, kcache, vcache, q_out=qo, max_new=max_new)
     torch.cuda.synchronize()
     for name, b, t in (("q_out", qb, qo), ("k cache", kb, kcache), ("v cache", vb, vcache), ("state k", skb, sk),
                        ("state v", svb, sv)):
