@@ -1567,8 +1567,11 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     const int prow = p_min + qi;
     // log-scale factor, kept > 0 so that masked -inf logits stay -inf
     const float fls = p.inv_ln_base > 0.f ? fmaxf(logf((float)prow + 1.f) * p.inv_ln_base, 1e-30f) : 1.f;
+    // q is scaled by amul once per block (scale, log2 e and the row's
+    // log-scale factor), so the scores come out of the matrix cores in the
+    // exp2 domain; bmul brings the bias there
     const float amul = p.scale_log2e * fls;
-    const float bsc = kLog2e / p.scale_log2e;   // 1 / scale: the bias in units of the raw dot product
+    const float bmul = kLog2e * fls;
     const bool wave_active = wave * 32 < ncols;
     const int rb = (prow - N + 1) & ~(CH - 1);
 
@@ -1797,7 +1800,9 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
                 O[st & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[st], P[st >> 2], O[st & 3], 0, 0, 0);
             } else {
                 const int q = st - 16;
-                if (q < KT) S[q] = f32x16{};
+                // scores start at -m0 (m0: the reference max, 0 before the
+                // column's first visible tile), so exp2(S) needs no subtraction
+                if (q < KT) S[q] = f32x16{} - (m == -INFINITY ? 0.f : m);
                 S[q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[st], qf[q >> 1], S[q & 1], 0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -1843,10 +1848,10 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
                     if (partial) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
-                            S[u][r] = fmaf(32 * u + r > elim ? (float)braw[r >> 3][7 - (r & 7)] : 0.f, bsc, S[u][r]);
+                            S[u][r] = fmaf(32 * u + r > elim ? (float)braw[r >> 3][7 - (r & 7)] : 0.f, bmul, S[u][r]);
                     } else {
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) S[u][r] = fmaf((float)braw[r >> 3][7 - (r & 7)], bsc, S[u][r]);
+                        for (int r = 0; r < 16; ++r) S[u][r] = fmaf((float)braw[r >> 3][7 - (r & 7)], bmul, S[u][r]);
                     }
                 }
                 if (edge) {
@@ -1866,8 +1871,11 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
         // in two chains.  (A v_dot2c sum over the bf16 values keeps numerator
         // and denominator on the same rounding, but those instructions stall
         // next to the other wave's MFMAs; full-causal workload 31.0 -> 30.2 ms.)
-        const float sa = amul;
+        // S holds scores minus m0 in the exp2 domain (see the matrix phase)
+        const float m0 = m == -INFINITY ? 0.f : m;
         float sum = 0.f;
+        // mu: the reference max the probabilities are taken against, as a
+        // shift from m0 (0 on the first pass)
         auto exps = [&](float mu, auto dma_b) __attribute__((always_inline)) {
             constexpr bool DB = decltype(dma_b)::value;
             float sm[2] = {0.f, 0.f};
@@ -1878,7 +1886,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
                     bf16x8 pb;
 #pragma unroll
                     for (int x = 0; x < 8; ++x) {
-                        const float e = fast_exp2(fmaf(S[u][8 * h2 + x], sa, -mu));
+                        const float e = fast_exp2(S[u][8 * h2 + x] - mu);   // mu = 0.f folds away
                         pb[x] = (__bf16)e;
                         sm[x & 1] += e;
                     }
@@ -1890,7 +1898,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
                 }
             sum = sm[0] + sm[1];
         };
-        exps(m == -INFINITY ? 0.f : m, std::integral_constant<bool, DMA>{});
+        exps(0.f, std::integral_constant<bool, DMA>{});
         o_scale = 1.f;
         // The reference max m only moves when the tile max exceeds it by more
         // than kRescaleSlack.  While the lane's probabilities sum to at most
@@ -1905,7 +1913,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
             for (int u = 0; u < KT; ++u)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mt = fmaxf(mt, S[u][r]);
-            mt *= amul;
+            mt += m0;
             mt = max_across_halves(mt);
             const bool grow = mt > m + kRescaleSlack;
             const float mn = grow ? mt : m;
@@ -1913,7 +1921,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
             m = mn;
             l *= alpha;
             o_scale = alpha;        // applied to O at the start of the next matrix phase
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) exps(m == -INFINITY ? 0.f : m, std::false_type{});
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) exps((m == -INFINITY ? 0.f : m) - m0, std::false_type{});
         }
         l += sum;
     };
@@ -1950,6 +1958,10 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
         for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(qf[k]));
     }
     wait_vmem();
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) qf[k][x] = (__bf16)((float)qf[k][x] * amul);
     lds_barrier();
 
     // ------------------------------------------------------------ phases 2t, 2t+1 for t = 0..n_it
