@@ -44,24 +44,25 @@ def log(*a):
 
 # HBM bytes per launch of each leg's dominant kernel: rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
 # (factors from a plain 1 GiB device copy under the same counters), keyed by leg and by the sha256
-# prefix of the kernel source the counters were taken on; any other source reports null.  The decode
-# entries were measured on the previous source, whose decode and combine kernels compile to the same
-# machine code as this one's (only the prefill kernels changed).
+# prefix of the kernel source the counters were taken on; any other source reports null.  Entries of
+# kernels whose machine code this source leaves unchanged (function bodies compared) carry over: the
+# decode, combine and MXFP8 kernels since source ac1e0709a59684d1, the fused prefill variants since
+# 781af5c0d78d6ba2, and attn_prefill_pp_kernel<0> (c3, c2) since e25a2cfed1e9566b.
 PROFILED_TRAFFIC = {
-    ("c3", "781af5c0d78d6ba2"): 6540542 * 1024 * 2 + 1048576 * 1024,
-    ("c2", "781af5c0d78d6ba2"): 507306 * 1024 * 2 + 131307 * 1024,
-    ("c3_fused_on_chip", "781af5c0d78d6ba2"): 2873850 * 1024 * 2 + 1048740 * 1024,
-    ("c2_fused_on_chip", "781af5c0d78d6ba2"): 145285 * 1024 * 2 + 132533 * 1024,
-    ("c3_fused_workspace", "781af5c0d78d6ba2"): 6296394 * 1024 * 2 + 5248363 * 1024,
-    ("c2_fused_workspace", "781af5c0d78d6ba2"): 529767 * 1024 * 2 + 656038 * 1024,
-    ("c4w/head-major", "781af5c0d78d6ba2"): 578556 * 1024 * 2 + 9216 * 1024,
-    ("c4f/head-major", "781af5c0d78d6ba2"): 1225724 * 1024 * 2 + 9216 * 1024,
-    ("c5/head-major", "781af5c0d78d6ba2"): 524484 * 1024 * 2 + 2064 * 1024,
-    ("c4f_paged64/head-major", "781af5c0d78d6ba2"): 1163403 * 1024 * 2 + 9218 * 1024,
-    ("c4f_mxfp8/head-major", "781af5c0d78d6ba2"): 654406 * 1024 * 2 + 9216 * 1024,
-    ("c4f_mxfp8_logits/head-major", "781af5c0d78d6ba2"): 654449 * 1024 * 2 + 9216 * 1024,
-    ("c5_mxfp8/head-major", "781af5c0d78d6ba2"): 270642 * 1024 * 2 + 2064 * 1024,
-    ("c5_mxfp8_logits/head-major", "781af5c0d78d6ba2"): 270641 * 1024 * 2 + 2064 * 1024,
+    ("c3", "df79a6c97489fa01"): 6530915 * 1024 * 2 + 1048577 * 1024,
+    ("c2", "df79a6c97489fa01"): 508398 * 1024 * 2 + 131455 * 1024,
+    ("c3_fused_on_chip", "df79a6c97489fa01"): 2873850 * 1024 * 2 + 1048740 * 1024,
+    ("c2_fused_on_chip", "df79a6c97489fa01"): 145285 * 1024 * 2 + 132533 * 1024,
+    ("c3_fused_workspace", "df79a6c97489fa01"): 6296394 * 1024 * 2 + 5248363 * 1024,
+    ("c2_fused_workspace", "df79a6c97489fa01"): 529767 * 1024 * 2 + 656038 * 1024,
+    ("c4w/head-major", "df79a6c97489fa01"): 578556 * 1024 * 2 + 9216 * 1024,
+    ("c4f/head-major", "df79a6c97489fa01"): 1225724 * 1024 * 2 + 9216 * 1024,
+    ("c5/head-major", "df79a6c97489fa01"): 524484 * 1024 * 2 + 2064 * 1024,
+    ("c4f_paged64/head-major", "df79a6c97489fa01"): 1163403 * 1024 * 2 + 9218 * 1024,
+    ("c4f_mxfp8/head-major", "df79a6c97489fa01"): 654406 * 1024 * 2 + 9216 * 1024,
+    ("c4f_mxfp8_logits/head-major", "df79a6c97489fa01"): 654449 * 1024 * 2 + 9216 * 1024,
+    ("c5_mxfp8/head-major", "df79a6c97489fa01"): 270642 * 1024 * 2 + 2064 * 1024,
+    ("c5_mxfp8_logits/head-major", "df79a6c97489fa01"): 270641 * 1024 * 2 + 2064 * 1024,
 }
 
 

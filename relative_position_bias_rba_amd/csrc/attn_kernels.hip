@@ -1284,9 +1284,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(const AttnPar
 //   group 0: phase 2t   MFMA [PV(t-1), QK(t)]   phase 2t+1 VALU [softmax(t)]
 //   group 1: phase 2t   VALU [softmax(t-1)]     phase 2t+1 MFMA [PV(t-1), QK(t)]
 // Each group runs its own copy of the phase loop with its roles fixed at
-// compile time.  All staging is global -> LDS DMA issued by group 1 in bursts
-// between the parts of its even-phase softmax (the matrix group's phase is the
-// longer one) and awaited at the end of the following odd phase: K(t+1), V(t) and the bias windows of both groups
+// compile time.  All staging is global -> LDS DMA issued by group 1 during
+// its even-phase softmax (one burst at its start, or four bursts spread over
+// it in the fused variants) and awaited at the end of the
+// following odd phase: K(t+1), V(t) and the bias windows of both groups
 // (group 0's for tile t+1, group 1's for tile t).  V is kept row-major in LDS
 // (16-byte chunks XOR-swizzled by row) and read as the PV A-operand with the
 // LDS transpose read, so it never passes through registers.  LDS regions are
@@ -1810,8 +1811,8 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
     };
     // Vector phase: bias, mask, running max and exponentials of tile t
     // (sequence index), key tile kt.
-    // With DMA the group issues this phase's staging instructions in four
-    // bursts spread over the softmax.
+    // With DMA the group issues this phase's staging instructions in one burst
+    // at its start (FK = 0) or in four bursts spread over the softmax.
     auto softmax = [&](int t, int kt, auto dma_c) __attribute__((always_inline)) {
         constexpr bool DMA = decltype(dma_c)::value;
         auto burst = [&](int s0, int s1) __attribute__((always_inline)) {
@@ -1825,7 +1826,10 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
         if constexpr (ONC) {
             if (band) bias_tile<FK, SWD>(p, sB, b, hkv, t0, nrows, p_min - j0 - (N - 1), wave, lane);
         }
-        burst(0, 6);
+        // the kernel reading R: all in one burst (full causal 29.29 -> 29.01 ms,
+        // A/B); the fused variants keep four bursts spread over the softmax
+        // (one burst made them 1-2 % slower)
+        burst(0, FK == 0 ? NSLOT : 6);
         const bool edge = !((j0 + N - 1 <= p_min) && (W == 0 || p_max - j0 < W));
         float mt = -INFINITY;
         if (band || edge) {
@@ -1865,7 +1869,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        burst(6, 11);
+        if constexpr (FK != 0) burst(6, 11);
         // Probabilities against the current reference max m (exp2 domain),
         // rounded to bf16 for the PV product; the row sum adds the fp32 values
         // in two chains.  (A v_dot2c sum over the bf16 values keeps numerator
@@ -1891,7 +1895,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_pp_kernel(const AttnParam
                         sm[x & 1] += e;
                     }
                     P[2 * u + h2] = pb;
-                    if constexpr (DB) {
+                    if constexpr (DB && FK != 0) {
                         if (u == 0 && h2 == 0) burst(11, 15);
                         if (u == 0 && h2 == 1) burst(15, NSLOT);
                     }
